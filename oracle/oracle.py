@@ -1,0 +1,165 @@
+"""ctypes wrapper of the fp64 oracle (test infrastructure only).
+
+Inputs may be any real numpy arrays of the documented shapes; they are widened
+to contiguous float64.  Outputs are float64 numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_OUT_DIR = os.path.join(_HERE, "_build")
+_LIB = os.path.join(_OUT_DIR, "liboracle.so")
+_lock = threading.Lock()
+_handle: Optional[ctypes.CDLL] = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle C source with gcc (-O2, OpenMP) into a shared library."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def _declare(h: ctypes.CDLL) -> ctypes.CDLL:
+    i = ctypes.c_int
+    d = ctypes.c_double
+    h.oracle_space_fwd.argtypes = [i] * 6 + [i, i, d] + [_DP] * 5
+    h.oracle_space_bwd.argtypes = [i] * 6 + [i, i, d] + [_DP] * 7
+    h.oracle_time_fwd.argtypes = [i] * 6 + [i, d] + [_DP] * 5
+    h.oracle_time_bwd.argtypes = [i] * 6 + [i, d] + [_DP] * 7
+    for f in (h.oracle_space_fwd, h.oracle_space_bwd, h.oracle_time_fwd, h.oracle_time_bwd):
+        f.restype = ctypes.c_int
+    h.oracle_set_threads.argtypes = [i]
+    h.oracle_set_threads.restype = None
+    h.oracle_max_threads.argtypes = []
+    h.oracle_max_threads.restype = ctypes.c_int
+    return h
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the oracle library (building it first if it does not exist).
+    With ``path`` given, load that file instead (used by planted-mistake tests)."""
+    global _handle
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _handle is None:
+            if not os.path.exists(_LIB):
+                build()
+            _handle = _declare(ctypes.CDLL(_LIB))
+        return _handle
+
+
+def set_threads(n: int) -> None:
+    load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(load().oracle_max_threads())
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_DP)
+
+
+def _dims(q, k):
+    B, T, N, Hq, D = q.shape
+    Hkv = k.shape[3]
+    if k.shape != (B, T, N, Hkv, D):
+        raise ValueError("k shape %s does not match q shape %s" % (k.shape, q.shape))
+    return B, T, N, Hq, Hkv, D
+
+
+def _check(rc: int, what: str):
+    if rc == -1:
+        raise ValueError("oracle %s: invalid arguments" % what)
+    if rc == -2:
+        raise ValueError("oracle %s: a query sees no key" % what)
+    if rc != 0:
+        raise RuntimeError("oracle %s: rc=%d" % (what, rc))
+
+
+def space_fwd(q, k, v, agent_begin: int = 0, agent_count: int = 0, scale: float = 0.0,
+              lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Space attention forward: returns (o, lse) in float64."""
+    h = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, N, Hq, Hkv, D = _dims(q, k)
+    o = np.zeros_like(q)
+    lse = np.zeros((B, T, N, Hq))
+    _check(h.oracle_space_fwd(B, T, N, Hq, Hkv, D, agent_begin, agent_count, scale,
+                              _p(q), _p(k), _p(v), _p(o), _p(lse)), "space_fwd")
+    return o, lse
+
+
+def space_bwd(q, k, v, dout, agent_begin: int = 0, agent_count: int = 0, scale: float = 0.0,
+              lib: Optional[ctypes.CDLL] = None):
+    """Space attention backward: returns (dq, dk, dv) in float64."""
+    h = lib or load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, T, N, Hq, Hkv, D = _dims(q, k)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    _check(h.oracle_space_bwd(B, T, N, Hq, Hkv, D, agent_begin, agent_count, scale,
+                              _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv)), "space_bwd")
+    return dq, dk, dv
+
+
+def time_fwd(q, k, v, window: int = 0, scale: float = 0.0,
+             lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Causal sliding-window time attention forward: returns (o, lse)."""
+    h = lib or load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, N, Hq, Hkv, D = _dims(q, k)
+    o = np.zeros_like(q)
+    lse = np.zeros((B, T, N, Hq))
+    _check(h.oracle_time_fwd(B, T, N, Hq, Hkv, D, window, scale,
+                             _p(q), _p(k), _p(v), _p(o), _p(lse)), "time_fwd")
+    return o, lse
+
+
+def time_bwd(q, k, v, dout, window: int = 0, scale: float = 0.0,
+             lib: Optional[ctypes.CDLL] = None):
+    """Causal sliding-window time attention backward: returns (dq, dk, dv)."""
+    h = lib or load()
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, T, N, Hq, Hkv, D = _dims(q, k)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    _check(h.oracle_time_bwd(B, T, N, Hq, Hkv, D, window, scale,
+                             _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv)), "time_bwd")
+    return dq, dk, dv
+
+
+def fwd(w, q, k, v, scale: float = 0.0, lib=None):
+    """Forward of workload ``w`` (a configs.Workload-like object)."""
+    if w.op == "space":
+        return space_fwd(q, k, v, w.agent_begin, w.agent_count, scale, lib=lib)
+    return time_fwd(q, k, v, w.window, scale, lib=lib)
+
+
+def bwd(w, q, k, v, dout, scale: float = 0.0, lib=None):
+    """Backward of workload ``w``."""
+    if w.op == "space":
+        return space_bwd(q, k, v, dout, w.agent_begin, w.agent_count, scale, lib=lib)
+    return time_bwd(q, k, v, dout, w.window, scale, lib=lib)
