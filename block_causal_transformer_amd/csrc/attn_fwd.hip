@@ -1,0 +1,286 @@
+// Flash-style forward of space and time attention, bf16 in/out, head_dim 64,
+// for gfx950 (MI355X).
+//
+// Open Dreamer articles (pro.edgex.exchange, fr-FR edition): section
+// "Architecture" (space layers inside one timestep block, causal time layers
+// across frames, world tokens cannot read the agent token) and section
+// "Configuration d'entraînement" (GQA 30 query heads over 3 KV heads, 192-step
+// sliding window for time attention).  Mixed precision follows the section
+// "Ingénierie de la stabilité": bf16 attention inputs, fp32 statistics.
+//
+// Work decomposition.  One attention problem is a (unit, KV head g) pair: a
+// unit is a block (space: positions = the N tokens of one frame) or a token
+// slot (time: positions = the T frames).  Its G = Hq/Hkv query heads are
+// folded into rows r = position * G + head-in-group, so that the K/V of the
+// group, staged once in LDS, serve all G heads.  A workgroup (4 waves) owns a
+// contiguous row range of one problem; each wave takes 64-row chunks and
+// sweeps the visible keys in 32-key steps.
+//
+// Per step and wave: S^T (keys x queries) = K Q^T on MFMA with K from LDS and
+// Q^T from registers, so every lane holds one query column and the row
+// statistics need only a 4-lane reduction; online softmax in the log2 domain
+// with a lazy rescale (the running reference max is moved only when a new
+// score exceeds it by more than 2^8, which keeps exp2 arguments <= 8);
+// O^T += V^T P^T on MFMA with V^T from LDS.  Fully masked key steps are never
+// visited (causal and window ranges), and per-element masks are applied only
+// on steps that straddle a mask edge.
+#include "bca_device.h"
+#include "bca_kernels.h"
+
+namespace bca {
+
+namespace {
+
+constexpr int KMAX = 320;      // keys resident in LDS per pass
+constexpr int QCH = 64;        // query rows per wave and chunk
+constexpr int NQT = QCH / 16;  // 16-column query tiles per chunk
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+
+struct FwdParams {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  int op, T, N, Hq, Hkv, G, L, units, rows;
+  int window, agent_begin, agent_count;
+  float scale_log2;
+  int splits, rows_per_split;
+};
+
+// V^T is stored with keys permuted inside each group of 32 so that the 8 keys
+// a lane feeds to one PV MFMA are contiguous: key 32a + 16h + 4g + j sits at
+// position 32a + 8g + 4h + j.
+__device__ __forceinline__ int vt_perm(int key) {
+  return (key & ~31) | (((key >> 2) & 3) << 3) | (((key >> 4) & 1) << 2) | (key & 3);
+}
+
+__device__ __forceinline__ int k_off(int row, int chunk) {  // sK: [KMAX][64], 16B chunks xor-swizzled
+  return row * 64 + ((chunk ^ (row & 7)) << 3);
+}
+
+__device__ __forceinline__ int vt_off(int d, int pos) {  // sVT: [64][KMAX]
+  return d * KMAX + ((((pos >> 3) ^ (d & 7))) << 3) + (pos & 7);
+}
+
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 sK[KMAX * 64];
+  __shared__ __attribute__((aligned(16))) bf16 sVT[64 * KMAX];
+
+  int ug, split;
+  xcd_remap(blockIdx.x, p.units * p.Hkv, p.splits, ug, split);
+  const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
+  const UnitGeom gq = unit_geom(p.op, u, p.T, p.N, p.Hq, 64);
+  const UnitGeom gk = unit_geom(p.op, u, p.T, p.N, p.Hkv, 64);
+  const UnitGeom gl = unit_geom(p.op, u, p.T, p.N, p.Hq, 1);
+  const MaskDesc md{p.op, p.L, p.window, p.agent_begin, p.agent_count};
+  const bf16* kbase = p.k + gk.base + g * 64;
+  const bf16* vbase = p.v + gk.base + g * 64;
+  const bf16* qbase = p.q + gq.base + (int64_t)g * p.G * 64;
+  bf16* obase = p.o + gq.base + (int64_t)g * p.G * 64;
+  float* lbase = p.lse + gl.base + g * p.G;
+
+  const int row0 = split * p.rows_per_split;
+  const int row1 = min(p.rows, row0 + p.rows_per_split);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int nkb = (p.L + KMAX - 1) / KMAX;
+  const int nch = (row1 - row0 + QCH - 1) / QCH;
+  const int passes = (nch + 3) >> 2;
+  const int G = p.G;
+
+  for (int pass = 0; pass < passes; ++pass) {
+    const int ch = pass * 4 + wave;
+    const bool active = ch < nch;
+    const int r0 = row0 + ch * QCH;
+
+    // Q^T operands, query positions and state for this chunk
+    bf16x8 qreg[NQT][2];
+    int qpos[NQT];
+    bool qvalid[NQT];
+    f32x4 acc[NQT][4];
+    float m[NQT], l[NQT];
+    int qlo = 0, qhi = 0;
+    if (active) {
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        const int r = r0 + qt * 16 + li;
+        qvalid[qt] = r < row1;
+        const int rr = qvalid[qt] ? r : row0;
+        qpos[qt] = rr / G;
+        const int hh = rr - qpos[qt] * G;
+        const bf16* src = qbase + qpos[qt] * gq.pos_stride + hh * 64 + lg * 8;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) qreg[qt][s] = qvalid[qt] ? ld_global16(src + s * 32) : zero8();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[qt] = -INFINITY;
+        l[qt] = 0.f;
+      }
+      qlo = r0 / G;
+      qhi = (min(r0 + QCH, row1) - 1) / G;
+    }
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int key0 = kb * KMAX;
+      const int kn = min(KMAX, p.L - key0);
+      if (nkb > 1 || pass == 0) {
+        if (nkb > 1) __syncthreads();
+        const int lp = (kn + 31) & ~31;
+        for (int idx = tid; idx < lp * 8; idx += 256) {
+          const int r = idx >> 3, c = idx & 7;
+          bf16x8 kv = zero8(), vv = zero8();
+          if (r < kn) {
+            kv = ld_global16(kbase + (int64_t)(key0 + r) * gk.pos_stride + c * 8);
+            vv = ld_global16(vbase + (int64_t)(key0 + r) * gk.pos_stride + c * 8);
+          }
+          st_lds16(sK + k_off(r, c), kv);
+          const int pp = vt_perm(r);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sVT[vt_off(c * 8 + e, pp)] = vv[e];
+        }
+        __syncthreads();
+      }
+      if (!active) continue;
+
+      int klo, khi;
+      key_range(md, qlo, qhi, klo, khi);
+      klo = max(klo, key0);
+      khi = min(khi, key0 + kn);
+      if (klo >= khi) continue;
+      const int st0 = (klo - key0) >> 5, st1 = (khi - key0 + 31) >> 5;
+      for (int st = st0; st < st1; ++st) {
+        const int kabs = key0 + st * 32;
+        // S^T tiles: rows = 16 keys (two halves of the step), columns = queries
+        f32x4 sc[NQT][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kr = st * 32 + h * 16 + li;
+          const bf16x8 k0 = ld_lds16(sK + k_off(kr, lg));
+          const bf16x8 k1 = ld_lds16(sK + k_off(kr, 4 + lg));
+#pragma unroll
+          for (int qt = 0; qt < NQT; ++qt) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = mfma16(k0, qreg[qt][0], z);
+            sc[qt][h] = mfma16(k1, qreg[qt][1], z);
+          }
+        }
+        if (!tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
+#pragma unroll
+          for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+              {
+                // a select, not a conditional store: hipcc dropped conditional
+                // element stores into this array of vectors
+                const bool vis = visible(md, qpos[qt], kabs + h * 16 + lg * 4 + j);
+                const float cur = sc[qt][h][j];
+                sc[qt][h][j] = vis ? cur : -INFINITY;
+              }
+        }
+        // online softmax with a lazy reference max (log2 domain)
+        float mx[NQT];
+        bool grow = false;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+          float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
+          float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
+          mx[qt] = group4_max(fmaxf(a, b)) * p.scale_log2;
+          grow |= mx[qt] > m[qt] + kRescaleThreshold;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+          for (int qt = 0; qt < NQT; ++qt) {
+            const float mn = fmaxf(m[qt], mx[qt]);
+            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m[qt] - mn);
+            l[qt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[qt][dt] *= alpha;
+            m[qt] = mn;
+          }
+        }
+        bf16x8 pb[NQT];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+          const float mref = (m[qt] == -INFINITY) ? 0.f : m[qt];
+          f32x4 e0, e1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            e0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -mref));
+            e1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -mref));
+          }
+          l[qt] += (e0[0] + e0[1]) + (e0[2] + e0[3]) + (e1[0] + e1[1]) + (e1[2] + e1[3]);
+          pb[qt] = pack8(e0, e1);
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8 vt = ld_lds16(sVT + vt_off(dt * 16 + li, st * 32 + lg * 8));
+#pragma unroll
+          for (int qt = 0; qt < NQT; ++qt) acc[qt][dt] = mfma16(vt, pb[qt], acc[qt][dt]);
+        }
+      }
+    }
+
+    if (active) {
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) {
+        const float lt = group4_sum(l[qt]);
+        if (!qvalid[qt]) continue;
+        const int r = r0 + qt * 16 + li;
+        const int hh = r - qpos[qt] * G;
+        const float inv = 1.f / lt;
+        bf16* dst = obase + qpos[qt] * gq.pos_stride + hh * 64 + lg * 4;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x4 o4 = pack4(acc[qt][dt] * inv);
+          *reinterpret_cast<u32x2*>(dst + dt * 16) = __builtin_bit_cast(u32x2, o4);
+        }
+        if (lg == 0) lbase[qpos[qt] * gl.pos_stride + hh] = (m[qt] + __log2f(lt)) * kLn2;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream) {
+  FwdParams p;
+  p.q = static_cast<const bf16*>(q);
+  p.k = static_cast<const bf16*>(k);
+  p.v = static_cast<const bf16*>(v);
+  p.o = static_cast<bf16*>(o);
+  p.lse = lse;
+  p.op = d.op;
+  p.T = d.T;
+  p.N = d.N;
+  p.Hq = d.Hq;
+  p.Hkv = d.Hkv;
+  p.G = d.Hq / d.Hkv;
+  p.L = d.op == OP_SPACE ? d.N : d.T;
+  p.units = d.op == OP_SPACE ? d.B * d.T : d.B * d.N;
+  p.rows = p.L * p.G;
+  p.window = d.window;
+  p.agent_begin = d.agent_begin;
+  p.agent_count = d.agent_count;
+  p.scale_log2 = d.scale * kLog2e;
+  // Split each problem's rows over several workgroups so that the grid
+  // covers the 256 CUs about three times over (2 workgroups per CU fit).
+  const int problems = p.units * p.Hkv;
+  const int chunks = (p.rows + QCH - 1) / QCH;
+  int splits = (int)((3 * 512 + problems - 1) / problems);
+  splits = max(1, min(splits, (chunks + 3) / 4));
+  int per = (chunks + splits - 1) / splits;
+  per = ((per + 3) / 4) * 4;  // whole passes of 4 chunks
+  p.rows_per_split = per * QCH;
+  p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
+  const long grid = (long)problems * p.splits;
+  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace bca

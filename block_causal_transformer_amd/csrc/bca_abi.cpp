@@ -1,0 +1,199 @@
+// C ABI shim: host-side validation, kernel selection and error reporting for
+// the declarations in include/bca.h.  Validation is synchronous, touches no
+// device memory and happens before any launch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "bca.h"
+#include "bca_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Fills `d` from the descriptors; returns BCA_OK or an error status.
+int validate(int op, const bca_shape* s, const bca_mask* m, bca::AttnDims* d) {
+  if (!s || !m) return fail(BCA_ERR_INVALID_ARG, "shape or mask descriptor is NULL");
+  if (s->B <= 0 || s->T <= 0 || s->N <= 0 || s->Hq <= 0 || s->Hkv <= 0 || s->D <= 0)
+    return fail(BCA_ERR_INVALID_ARG, "non-positive size (B=%d T=%d N=%d Hq=%d Hkv=%d D=%d)",
+                s->B, s->T, s->N, s->Hq, s->Hkv, s->D);
+  if (s->Hq % s->Hkv != 0)
+    return fail(BCA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", s->Hq, s->Hkv);
+  if (s->dtype != BCA_BF16 && s->dtype != BCA_F32)
+    return fail(BCA_ERR_UNSUPPORTED, "unknown dtype %d", s->dtype);
+  if (s->D != 32 && s->D != 64) return fail(BCA_ERR_UNSUPPORTED, "head_dim %d (need 32 or 64)", s->D);
+  // element counts must fit the kernels' 64-bit offsets and 32-bit grids
+  const double elems = (double)s->B * s->T * s->N * s->Hq * s->D;
+  if (elems > 4.0e15) return fail(BCA_ERR_INVALID_ARG, "tensor too large (%.3g elements)", elems);
+  const double rows = (double)s->B * s->T * s->N * s->Hq;
+  if (rows / 128.0 > 2.0e9) return fail(BCA_ERR_INVALID_ARG, "too many rows for the launch grid");
+  if (m->agent_begin < 0 || m->agent_count < 0 ||
+      (int64_t)m->agent_begin + m->agent_count > s->N)
+    return fail(BCA_ERR_INVALID_ARG, "agent range [%d, %d+%d) not inside [0, N=%d]",
+                m->agent_begin, m->agent_begin, m->agent_count, s->N);
+  if (m->window < 0) return fail(BCA_ERR_INVALID_ARG, "window %d < 0", m->window);
+  if (!(isfinite(m->softmax_scale))) return fail(BCA_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (op == BCA_OP_SPACE) {
+    if (m->causal != 0) return fail(BCA_ERR_UNSUPPORTED, "space attention is not causal (causal=%d)", m->causal);
+    if (m->window != 0) return fail(BCA_ERR_UNSUPPORTED, "space attention takes no window (window=%d)", m->window);
+  } else {
+    if (m->causal != 1) return fail(BCA_ERR_UNSUPPORTED, "time attention must be causal (causal=%d)", m->causal);
+  }
+  d->op = op;
+  d->B = s->B;
+  d->T = s->T;
+  d->N = s->N;
+  d->Hq = s->Hq;
+  d->Hkv = s->Hkv;
+  d->D = s->D;
+  d->dtype = s->dtype;
+  d->window = op == BCA_OP_TIME ? m->window : 0;
+  d->agent_begin = op == BCA_OP_SPACE ? m->agent_begin : 0;
+  d->agent_count = op == BCA_OP_SPACE ? m->agent_count : 0;
+  d->scale = m->softmax_scale > 0.f ? m->softmax_scale : 1.0f / sqrtf((float)s->D);
+  return BCA_OK;
+}
+
+int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) return fail(BCA_ERR_INVALID_ARG, "pointer '%s' is NULL", names[i]);
+    if (!aligned16(ptrs[i])) return fail(BCA_ERR_INVALID_ARG, "pointer '%s' is not 16-byte aligned", names[i]);
+  }
+  return BCA_OK;
+}
+
+size_t workspace_bytes(const bca::AttnDims& d) {
+  if (bca::bwd_uses_mfma(d)) return 0;
+  return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return BCA_OK;
+  return fail(BCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int do_fwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
+           const void* v, void* o, float* lse, void* stream) {
+  bca::AttnDims d;
+  int st = validate(op, shape, mask, &d);
+  if (st) return st;
+  const char* names[] = {"q", "k", "v", "o", "lse"};
+  const void* ptrs[] = {q, k, v, o, lse};
+  st = check_ptrs(names, ptrs, 5);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = bca::fwd_uses_mfma(d) ? bca::launch_attn_fwd_bf16(d, q, k, v, o, lse, s)
+                                       : bca::launch_attn_fwd_generic(d, q, k, v, o, lse, s);
+  st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_fwd launch" : "time_attn_fwd launch");
+  if (st == BCA_OK) g_last_error.clear();
+  return st;
+}
+
+int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
+           const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk,
+           void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  bca::AttnDims d;
+  int st = validate(op, shape, mask, &d);
+  if (st) return st;
+  const char* names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"};
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  st = check_ptrs(names, ptrs, 9);
+  if (st) return st;
+  const size_t need = workspace_bytes(d);
+  if (need > 0) {
+    if (ws_bytes < need)
+      return fail(BCA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu required",
+                  ws_bytes, need);
+    if (!workspace || !aligned16(workspace))
+      return fail(BCA_ERR_INVALID_ARG, "workspace is NULL or not 16-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = bca::bwd_uses_mfma(d)
+                     ? bca::launch_attn_bwd_bf16(d, q, k, v, o, lse, dout, dq, dk, dv, s)
+                     : bca::launch_attn_bwd_generic(d, q, k, v, o, lse, dout, dq, dk, dv,
+                                                    static_cast<float*>(workspace), s);
+  st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_bwd launch" : "time_attn_bwd launch");
+  if (st == BCA_OK) g_last_error.clear();
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int space_attn_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
+                   const void* v, void* o, float* lse, void* stream) {
+  return do_fwd(BCA_OP_SPACE, shape, mask, q, k, v, o, lse, stream);
+}
+
+int time_attn_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
+                  const void* v, void* o, float* lse, void* stream) {
+  return do_fwd(BCA_OP_TIME, shape, mask, q, k, v, o, lse, stream);
+}
+
+int space_attn_bwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
+                   const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                   void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return do_bwd(BCA_OP_SPACE, shape, mask, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                workspace_bytes, stream);
+}
+
+int time_attn_bwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
+                  const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                  void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return do_bwd(BCA_OP_TIME, shape, mask, q, k, v, o, lse, dout, dq, dk, dv, workspace,
+                workspace_bytes, stream);
+}
+
+size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape) {
+  if (op != BCA_OP_SPACE && op != BCA_OP_TIME) return 0;
+  bca_mask m;
+  m.causal = op == BCA_OP_TIME ? 1 : 0;
+  m.window = 0;
+  m.agent_begin = 0;
+  m.agent_count = 0;
+  m.softmax_scale = 0.f;
+  bca::AttnDims d;
+  const std::string saved = g_last_error;
+  if (validate(op, shape, &m, &d) != BCA_OK) {
+    g_last_error = saved;
+    return 0;
+  }
+  return workspace_bytes(d);
+}
+
+const char* bca_status_string(int status) {
+  switch (status) {
+    case BCA_OK: return "BCA_OK";
+    case BCA_ERR_INVALID_ARG: return "BCA_ERR_INVALID_ARG";
+    case BCA_ERR_UNSUPPORTED: return "BCA_ERR_UNSUPPORTED";
+    case BCA_ERR_HIP: return "BCA_ERR_HIP";
+    default: return "BCA_UNKNOWN_STATUS";
+  }
+}
+
+const char* bca_last_error(void) { return g_last_error.c_str(); }
+
+int bca_abi_version(void) { return BCA_ABI_VERSION; }
+
+}  // extern "C"

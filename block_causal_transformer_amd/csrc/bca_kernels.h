@@ -1,0 +1,46 @@
+// Internal launch interface between the C ABI shim and the HIP kernels.
+// Shapes arrive here already validated by the shim.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace bca {
+
+struct AttnDims {
+  int op;                 // 0 = space, 1 = time
+  int B, T, N, Hq, Hkv, D;
+  int dtype;              // 0 = bf16, 1 = fp32
+  int window;             // time: 0 = unbounded causal
+  int agent_begin, agent_count;  // space
+  float scale;            // softmax scale (> 0)
+};
+
+// Largest sequence length (tokens for space, frames for time) the
+// LDS-resident MFMA backward handles; longer problems take the generic path.
+constexpr int kMfmaBwdMaxLen = 320;
+
+// MFMA kernels: bf16, D = 64.
+hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k, const void* v,
+                                void* o, float* lse, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k, const void* v,
+                                const void* o, const float* lse, const void* dout, void* dq,
+                                void* dk, void* dv, hipStream_t stream);
+
+// Generic VALU kernels: fp32 or bf16 storage, D = 32 or 64, any length.
+hipError_t launch_attn_fwd_generic(const AttnDims& d, const void* q, const void* k,
+                                   const void* v, void* o, float* lse, hipStream_t stream);
+hipError_t launch_attn_bwd_generic(const AttnDims& d, const void* q, const void* k,
+                                   const void* v, const void* o, const float* lse,
+                                   const void* dout, void* dq, void* dk, void* dv,
+                                   float* delta_ws, hipStream_t stream);
+
+// True when the backward of these dims runs on the MFMA kernel.
+inline bool bwd_uses_mfma(const AttnDims& d) {
+  const int L = d.op == 0 ? d.N : d.T;
+  return d.dtype == 0 && d.D == 64 && L <= kMfmaBwdMaxLen;
+}
+
+inline bool fwd_uses_mfma(const AttnDims& d) { return d.dtype == 0 && d.D == 64; }
+
+}  // namespace bca

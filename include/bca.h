@@ -1,0 +1,149 @@
+/*
+ * bca.h -- block-causal attention for AMD MI355X (gfx950): C ABI.
+ *
+ * The operations are the two attention kinds of the block-causal transformer
+ * backbone shared by the Open Dreamer tokenizer and dynamics model (Open
+ * Dreamer articles, pro.edgex.exchange fr-FR edition):
+ *
+ *  - space attention: section "Architecture" -- space layers move
+ *    information among the tokens of one timestep block, and world-model
+ *    tokens cannot read the agent token; section "Configuration
+ *    d'entraînement" -- 30 query heads over 3 KV heads (grouped-query
+ *    attention) at d_model 1920, i.e. head_dim 64.
+ *  - time attention: section "Architecture" -- causal time layers move
+ *    information across frames; section "Configuration d'entraînement" --
+ *    a 192-step sliding window.
+ *
+ * Definition (softmax scale s, G = Hq / Hkv, query head h reads KV head
+ * h / G).  A "unit" is one (b, t) block for space attention and one (b, n)
+ * token slot for time attention; positions inside a unit are tokens
+ * (space) or frames (time).  For query position i of head h:
+ *     z_ij = s * <q_i,h , k_j,h/G>  for j in vis(i)
+ *     O_i,h = sum_j softmax_j(z_i.) v_j,h/G,  LSE_i,h = ln sum_j exp(z_ij)
+ * with
+ *     space: vis(i) = { j : not agent(j) or agent(i) },
+ *            agent(j) <=> agent_begin <= j < agent_begin + agent_count;
+ *     time:  vis(t) = { t' : t' <= t and (window == 0 or t - t' <= window-1) }
+ *            (the window counts the current frame).
+ * The backward returns the gradients of sum(O * dO) with respect to q, k, v
+ * (dK and dV of a KV head summed over the G query heads of its group).
+ *
+ * Layout (all row-major, contiguous):
+ *     q, o, dout, dq : (B, T, N, Hq,  D)   dtype
+ *     k, v, dk, dv   : (B, T, N, Hkv, D)   dtype
+ *     lse            : (B, T, N, Hq)       float32, natural log
+ * dtype is bf16 (BCA_BF16) or fp32 (BCA_F32); bf16 results are rounded to
+ * nearest even from fp32 accumulators.  Supported head_dim: 32 and 64.
+ *
+ * Pointers are device pointers (HIP device memory of the current device),
+ * 16-byte aligned.  The caller owns every buffer and keeps it alive until the
+ * work queued on `stream` has finished.  Outputs are overwritten, never
+ * accumulated, and must not alias inputs.  The library allocates no device
+ * memory and keeps no state between calls; calls are thread-safe.
+ *
+ * Errors: every argument is validated on the host before anything is
+ * launched; on failure nothing is written and a status is returned:
+ *     BCA_ERR_INVALID_ARG  null pointer, non-positive size, Hq % Hkv != 0,
+ *                          misaligned pointer, window < 0, agent range not
+ *                          inside [0, N], workspace too small, sizes beyond
+ *                          the 32-bit grid / 64-bit offset limits;
+ *     BCA_ERR_UNSUPPORTED  head_dim not 32 or 64, unknown dtype, causal or
+ *                          window set on the space op, causal == 0 on the
+ *                          time op;
+ *     BCA_ERR_HIP          the HIP runtime reported a launch error.
+ * bca_last_error() returns a human-readable detail of the calling thread's
+ * last failure.  Work is asynchronous on `stream` (a hipStream_t; NULL = the
+ * default stream); faults inside a kernel surface at the caller's next
+ * synchronization.  No exception, abort or print crosses this interface.
+ */
+#ifndef BCA_H
+#define BCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BCA_ABI_VERSION 1
+
+typedef enum {
+  BCA_OK = 0,
+  BCA_ERR_INVALID_ARG = 1,
+  BCA_ERR_UNSUPPORTED = 2,
+  BCA_ERR_HIP = 3
+} bca_status;
+
+typedef enum { BCA_BF16 = 0, BCA_F32 = 1 } bca_dtype;
+
+typedef enum { BCA_OP_SPACE = 0, BCA_OP_TIME = 1 } bca_op;
+
+/* Tensor sizes: batch, frames, tokens per frame, query heads, KV heads,
+ * head_dim, and the storage dtype (bca_dtype). */
+typedef struct {
+  int32_t B, T, N, Hq, Hkv, D;
+  int32_t dtype;
+} bca_shape;
+
+/* Mask descriptor.
+ *   causal        time op: must be 1 (t' <= t).  space op: must be 0.
+ *   window        time op: > 0 -> key frame t' visible iff t - t' <= window-1;
+ *                 0 -> unbounded causal.  space op: must be 0.
+ *   agent_begin,  space op: slots [agent_begin, agent_begin + agent_count)
+ *   agent_count   of every block are agent tokens, unreadable by the other
+ *                 (world) tokens; agent tokens read every slot.  count 0 = no
+ *                 isolation.  time op: validated, no effect (query and key
+ *                 always share a slot).
+ *   softmax_scale <= 0 -> 1/sqrt(D). */
+typedef struct {
+  int32_t causal;
+  int32_t window;
+  int32_t agent_begin;
+  int32_t agent_count;
+  float softmax_scale;
+} bca_mask;
+
+/* Space attention forward: writes o and lse.  Every query sees at least
+ * itself, so no row is empty. */
+int space_attn_fwd(const bca_shape* shape, const bca_mask* mask, const void* q,
+                   const void* k, const void* v, void* o, float* lse, void* stream);
+
+/* Space attention backward.  Inputs: q, k, v, the forward's o and lse, and
+ * dout = dL/dO.  Outputs: dq, dk, dv.  workspace: device scratch of at least
+ * bca_bwd_workspace_bytes(BCA_OP_SPACE, shape) bytes (may be NULL when that
+ * is 0); its contents on entry do not matter. */
+int space_attn_bwd(const bca_shape* shape, const bca_mask* mask, const void* q,
+                   const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Causal sliding-window time attention forward (per token slot). */
+int time_attn_fwd(const bca_shape* shape, const bca_mask* mask, const void* q,
+                  const void* k, const void* v, void* o, float* lse, void* stream);
+
+/* Causal sliding-window time attention backward; arguments as space_attn_bwd. */
+int time_attn_bwd(const bca_shape* shape, const bca_mask* mask, const void* q,
+                  const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace the backward of `op` needs for `shape` (0 when
+ * the LDS-resident MFMA backward runs; the fp32 Delta = rowsum(dO * O) buffer
+ * otherwise).  Returns 0 for an invalid shape. */
+size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape);
+
+/* Static string naming a status code. */
+const char* bca_status_string(int status);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* bca_last_error(void);
+
+/* BCA_ABI_VERSION of the loaded library. */
+int bca_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BCA_H */

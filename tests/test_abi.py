@@ -1,0 +1,146 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/bca.h, and rejects bad arguments on the host before any
+launch (fake device pointers are never dereferenced on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_causal_transformer_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bca.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ops.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(ops.EXPORTED) == set(names), names
+    raw = ctypes.CDLL(ops.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), "libbca.so does not export %s" % n
+
+
+def test_version_and_status_strings(lib):
+    assert ops.bca_abi_version() == ops.ABI_VERSION
+    assert ops.bca_status_string(0) == "BCA_OK"
+    assert ops.bca_status_string(1) == "BCA_ERR_INVALID_ARG"
+    assert ops.bca_status_string(2) == "BCA_ERR_UNSUPPORTED"
+    assert ops.bca_status_string(3) == "BCA_ERR_HIP"
+    assert ops.bca_status_string(99) == "BCA_UNKNOWN_STATUS"
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def good_shape(**kw):
+    d = dict(B=1, T=4, N=10, Hq=4, Hkv=2, D=64, dtype=ops.BCA_BF16)
+    d.update(kw)
+    return ops.BcaShape(d["B"], d["T"], d["N"], d["Hq"], d["Hkv"], d["D"], d["dtype"])
+
+
+def fwd_call(op, shape, mask, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    f = ops.space_attn_fwd if op == "space" else ops.time_attn_fwd
+    return f(shape, mask, *p)
+
+
+def bwd_call(op, shape, mask, ptrs=None, ws=None, ws_bytes=0):
+    p = ptrs or [FAKE] * 9
+    f = ops.space_attn_bwd if op == "space" else ops.time_attn_bwd
+    return f(shape, mask, *p, ws, ws_bytes)
+
+
+SPACE_MASK = ops.BcaMask(0, 0, 9, 1, 0.0)
+TIME_MASK = ops.BcaMask(1, 3, 0, 0, 0.0)
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("T", -1), ("N", 0), ("Hq", 0), ("Hkv", 0), ("D", 0)])
+def test_non_positive_sizes(lib, field, value):
+    for op, m in (("space", SPACE_MASK), ("time", TIME_MASK)):
+        assert fwd_call(op, good_shape(**{field: value}), m) == ops.BCA_ERR_INVALID_ARG
+        assert bwd_call(op, good_shape(**{field: value}), m) == ops.BCA_ERR_INVALID_ARG
+        assert "size" in ops.bca_last_error()
+
+
+def test_group_divisibility(lib):
+    assert fwd_call("space", good_shape(Hq=5, Hkv=2), SPACE_MASK) == ops.BCA_ERR_INVALID_ARG
+    assert "multiple" in ops.bca_last_error()
+
+
+@pytest.mark.parametrize("D", [16, 48, 128])
+def test_unsupported_head_dim(lib, D):
+    assert fwd_call("space", good_shape(D=D), SPACE_MASK) == ops.BCA_ERR_UNSUPPORTED
+    assert bwd_call("time", good_shape(D=D), TIME_MASK) == ops.BCA_ERR_UNSUPPORTED
+
+
+def test_unknown_dtype(lib):
+    assert fwd_call("space", good_shape(dtype=7), SPACE_MASK) == ops.BCA_ERR_UNSUPPORTED
+
+
+def test_null_and_misaligned_pointers(lib):
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = 0
+        assert fwd_call("space", good_shape(), SPACE_MASK, p) == ops.BCA_ERR_INVALID_ARG
+        assert "NULL" in ops.bca_last_error()
+        p[i] = FAKE + 8
+        assert fwd_call("time", good_shape(), TIME_MASK, p) == ops.BCA_ERR_INVALID_ARG
+        assert "aligned" in ops.bca_last_error()
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = 0
+        assert bwd_call("space", good_shape(), SPACE_MASK, p) == ops.BCA_ERR_INVALID_ARG
+
+
+def test_mask_descriptor_rules(lib):
+    s = good_shape()
+    # space op: no causality, no window
+    assert fwd_call("space", s, ops.BcaMask(1, 0, 0, 0, 0.0)) == ops.BCA_ERR_UNSUPPORTED
+    assert fwd_call("space", s, ops.BcaMask(0, 4, 0, 0, 0.0)) == ops.BCA_ERR_UNSUPPORTED
+    # time op must be causal
+    assert fwd_call("time", s, ops.BcaMask(0, 4, 0, 0, 0.0)) == ops.BCA_ERR_UNSUPPORTED
+    # window < 0
+    assert fwd_call("time", s, ops.BcaMask(1, -1, 0, 0, 0.0)) == ops.BCA_ERR_INVALID_ARG
+    # agent range outside [0, N]
+    for ab, ac in ((-1, 1), (9, 2), (0, -1), (11, 0)):
+        assert fwd_call("space", s, ops.BcaMask(0, 0, ab, ac, 0.0)) == ops.BCA_ERR_INVALID_ARG
+    # non-finite scale
+    assert fwd_call("space", s, ops.BcaMask(0, 0, 0, 0, float("nan"))) == ops.BCA_ERR_INVALID_ARG
+    assert fwd_call("space", s, ops.BcaMask(0, 0, 0, 0, float("inf"))) == ops.BCA_ERR_INVALID_ARG
+    assert fwd_call("space", None, SPACE_MASK) == ops.BCA_ERR_INVALID_ARG
+
+
+def test_workspace_query_and_check(lib):
+    # LDS-resident MFMA backward (bf16, D 64, <= 320 positions): no workspace
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=290)) == 0
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=256)) == 0
+    # generic backward: one fp32 Delta per (query, head)
+    s = good_shape(N=1432, T=2)
+    need = ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, s)
+    assert need == 1 * 2 * 1432 * 4 * 4
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(dtype=ops.BCA_F32)) == 1 * 4 * 10 * 4 * 4
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(B=0)) == 0
+    assert ops.bca_bwd_workspace_bytes(5, good_shape()) == 0
+    rc = bwd_call("space", s, ops.BcaMask(0, 0, 0, 0, 0.0), ws=FAKE, ws_bytes=need - 1)
+    assert rc == ops.BCA_ERR_INVALID_ARG and "workspace" in ops.bca_last_error()
+    rc = bwd_call("space", s, ops.BcaMask(0, 0, 0, 0, 0.0), ws=None, ws_bytes=need)
+    assert rc == ops.BCA_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        ops.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,111 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on
+the same seeded inputs, at the tolerances of the bf16 and fp32 paths.
+
+* every workload at a reduced unit count (whole units, several tiles, ragged
+  tails), compared element by element;
+* every workload at its full size, in the launch configuration the bench
+  uses, compared on sampled units (blocks or slots);
+* a ragged sweep over lengths, windows, head layouts and head_dim 32.
+"""
+import numpy as np
+import pytest
+
+from block_causal_transformer_amd import configs as C
+from block_causal_transformer_amd import gen
+
+import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def _needs_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+REDUCED = {
+    "1s": C.get("1s"),
+    "1t": C.get("1t"),
+    "2s": C.get("2s").with_(B=2, T=3),
+    "2t": C.get("2t").with_(B=2, N=3),
+    "2su": C.get("2su").with_(B=2, T=3),
+    "2tu": C.get("2tu").with_(B=2, N=3),
+    "3": C.get("3").with_(B=1, T=3),
+    "4": C.get("4").with_(N=3),
+    "5a": C.get("5a").with_(T=1),
+    "5b": C.get("5b").with_(T=1, Hq=4, Hkv=4),
+    "5c": C.get("5c").with_(N=5),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_parity_reduced(name):
+    _needs_gpu()
+    w = REDUCED[name]
+    print("case", name, w, flush=True)
+    inp = gen.make_inputs(w)
+    got = U.run_hip(w, inp)
+    want = U.run_oracle(w, inp)
+    print(U.assert_close(w, got, want, name))
+
+
+FULL_SAMPLES = {
+    "2s": [0, 77, 511],
+    "2t": [0, 300, 591],
+    "3": [0, 131, 255],
+    "4": [0, 145, 289],
+    "5a": [0, 15],
+    "5b": [7],
+    "5c": [0, 700, 1431],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SAMPLES))
+def test_parity_full_size_sampled(name):
+    _needs_gpu()
+    w = C.get(name)
+    print("case full", name, flush=True)
+    inp = gen.make_inputs(w)
+    got = U.run_hip(w, inp)
+    ws, inp_s, got_s = U.sample_units(w, got, inp, FULL_SAMPLES[name])
+    want = U.run_oracle(ws, inp_s)
+    print(U.assert_close(ws, got_s, want, name + " full"))
+
+
+RAGGED = []
+for N in (1, 2, 15, 17, 74, 290, 320, 321):
+    RAGGED.append(C.Workload("space_N%d" % N, "space", 1, 2, N, 6, 2, 64, "bf16", 0,
+                             N - 1, 1, 1.0, 7000 + N))
+for T, W in ((1, 4), (3, 0), (191, 192), (192, 192), (193, 192), (64, 1), (70, 4), (257, 0), (321, 16)):
+    RAGGED.append(C.Workload("time_T%d_W%d" % (T, W), "time", 1, T, 2, 6, 2, 64, "bf16", W,
+                             0, 0, 1.0, 8000 + T + W))
+RAGGED += [
+    C.Workload("space_mha", "space", 1, 2, 37, 4, 4, 64, "bf16", 0, 0, 2, 1.0, 9001),
+    C.Workload("space_agent_mid", "space", 2, 1, 40, 6, 3, 64, "bf16", 0, 17, 3, 1.0, 9002),
+    C.Workload("space_no_agent", "space", 1, 2, 50, 3, 1, 64, "bf16", 0, 0, 0, 1.0, 9003),
+    C.Workload("time_mha", "time", 1, 20, 3, 4, 4, 64, "bf16", 5, 0, 0, 1.0, 9004),
+    C.Workload("space_d32_bf16", "space", 1, 2, 33, 4, 2, 32, "bf16", 0, 32, 1, 1.0, 9005),
+    C.Workload("time_d32_bf16", "time", 1, 9, 3, 4, 2, 32, "bf16", 3, 0, 0, 1.0, 9006),
+    C.Workload("space_d64_f32", "space", 1, 2, 21, 4, 2, 64, "f32", 0, 20, 1, 1.0, 9007),
+    C.Workload("time_d64_f32", "time", 1, 12, 2, 4, 1, 64, "f32", 5, 0, 0, 1.0, 9008),
+]
+
+
+@pytest.mark.parametrize("w", RAGGED, ids=[w.name for w in RAGGED])
+def test_parity_ragged(w):
+    _needs_gpu()
+    print("case", w.name, flush=True)
+    inp = gen.make_inputs(w)
+    got = U.run_hip(w, inp)
+    want = U.run_oracle(w, inp)
+    print(U.assert_close(w, got, want, w.name))
+
+
+def test_parity_custom_scale():
+    _needs_gpu()
+    w = C.get("3").with_(B=1, T=1)
+    inp = gen.make_inputs(w)
+    got = U.run_hip(w, inp, scale=0.07)
+    want = U.run_oracle(w, inp, scale=0.07)
+    print(U.assert_close(w, got, want, "scale 0.07"))
