@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-causal attention hot path on one MI355X.
+
+One step = one pass of the dynamics model's attention at the Minecraft shape
+(Open Dreamer articles, pro.edgex.exchange fr-FR edition, sections
+"Architecture" and "Configuration d'entraînement"; 256 frames per GPU from
+section "Performance de calcul et stratégie mémoire"):
+
+  space layer: 256 blocks (4 sequences x 64 frames) of 290 tokens, 30 query
+               heads over 3 KV heads, head_dim 64, agent-token isolation:
+               forward + backward;
+  time layer:  256 frames x 290 token slots, causal, 192-step window, same
+               heads: forward + backward.
+
+Inputs are seeded synthetic bf16 tensors resident in HBM before the timed
+region.  ``value`` is algorithmic TFLOP/s over the whole step: 4*D FLOPs per
+visible (query, key, head) pair forward and 10*D backward; masked and padded
+work is never counted.  Per-op kernel durations come from HIP events on the
+stream the kernels run on.
+
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--no-cpu-baseline]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key: str):
+    """HBM bytes per launch of ``kernel_key`` from the committed rocprofv3
+    counter summary, or None when absent or taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#") or "=" not in line:
+                continue
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha") != source_digest():
+        return None
+    v = vals.get(kernel_key + ".bytes")
+    return float(v) if v else None
+
+
+def cpu_baseline(target_s: float = 12.0):
+    """Time the fp64 oracle on a bounded sample of the same step (whole
+    blocks of the space layer and whole slots of the time layer)."""
+    import numpy as np
+    from block_causal_transformer_amd import configs as C, gen
+    from oracle import oracle as O
+
+    def run(nb, ns):
+        ws = C.get("3").with_(B=1, T=nb)
+        wt = C.get("4").with_(N=ns)
+        xs, xt = gen.make_inputs(ws), gen.make_inputs(wt)
+        t0 = time.perf_counter()
+        O.fwd(ws, xs["q"], xs["k"], xs["v"])
+        O.bwd(ws, xs["q"], xs["k"], xs["v"], xs["dout"])
+        O.fwd(wt, xt["q"], xt["k"], xt["v"])
+        O.bwd(wt, xt["q"], xt["k"], xt["v"], xt["dout"])
+        dt = time.perf_counter() - t0
+        fl = sum(C.flops(w, d) for w in (ws, wt) for d in ("fwd", "bwd"))
+        return dt, fl
+
+    dt, fl = run(1, 1)
+    scale = max(1, min(64, int(target_s / max(dt, 1e-3))))
+    dt, fl = run(scale, scale)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.max_threads(),
+        "kind": "oracle",
+        "sample": "%d space blocks (290 tokens) + %d time slots (256 frames), fwd+bwd, fp64, %.1f s"
+                  % (scale, scale, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the op shards by block / slot with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_causal_transformer_amd import configs as C, gen, ops
+
+    if not os.path.exists(ops.LIB_PATH):
+        from block_causal_transformer_amd import build as hip_build
+        hip_build.build()
+    ops.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    ws, wt = C.get("3"), C.get("4")
+    bufs = {}
+    for w in (ws, wt):
+        x = gen.make_inputs(w)
+        b = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()}
+        del x
+        b["o"] = torch.empty_like(b["q"])
+        b["lse"] = torch.empty(w.lse_shape(), dtype=torch.float32, device=dev)
+        b["dq"] = torch.empty_like(b["q"])
+        b["dk"] = torch.empty_like(b["k"])
+        b["dv"] = torch.empty_like(b["v"])
+        b["shape"] = ops.make_shape(b["q"], b["k"])
+        b["mask"] = ops.make_mask(w.op, **ops.workload_kwargs(w))
+        need = ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE if w.op == "space" else ops.BCA_OP_TIME,
+                                           b["shape"])
+        b["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
+        b["ws_bytes"] = need
+        bufs[w.name] = b
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def call(name, direction):
+        b = bufs[name]
+        w = C.get(name)
+        if direction == "fwd":
+            f = ops.space_attn_fwd if w.op == "space" else ops.time_attn_fwd
+            rc = f(b["shape"], b["mask"], b["q"], b["k"], b["v"], b["o"], b["lse"], sp)
+        else:
+            f = ops.space_attn_bwd if w.op == "space" else ops.time_attn_bwd
+            rc = f(b["shape"], b["mask"], b["q"], b["k"], b["v"], b["o"], b["lse"], b["dout"],
+                   b["dq"], b["dk"], b["dv"], b["ws"], b["ws_bytes"], sp)
+        if rc != 0:
+            raise RuntimeError("%s %s: %s" % (name, direction, ops.bca_last_error()))
+
+    seq = [("3", "fwd"), ("3", "bwd"), ("4", "fwd"), ("4", "bwd")]
+    labels = {("3", "fwd"): "space_fwd", ("3", "bwd"): "space_bwd",
+              ("4", "fwd"): "time_fwd", ("4", "bwd"): "time_bwd"}
+
+    for _ in range(args.warmup):
+        for name, d in seq:
+            call(name, d)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        evs[s][0].record(stream)
+        for i, (name, d) in enumerate(seq):
+            call(name, d)
+            evs[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    per_op = {}
+    total_flops = 0.0
+    for i, key in enumerate(seq):
+        w = C.get(key[0])
+        ms = sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
+        fl = C.flops(w, key[1])
+        by = C.min_bytes(w, key[1])
+        total_flops += fl
+        per_op[labels[key]] = {
+            "ms": round(ms, 5),
+            "tflops": round(fl / ms / 1e9, 2),
+            "pct_mfma_peak": round(100.0 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+            "gbps": round(by / ms / 1e6, 1),
+            "pct_hbm_peak": round(100.0 * by / ms / 1e6 / PEAK_HBM_GBPS, 2),
+            "flop": fl,
+            "min_bytes": by,
+        }
+    ms_step = elapsed / args.steps * 1e3
+    value = total_flops * args.steps / elapsed / 1e12
+
+    # dominant kernel: the op with the largest time share
+    dom = max(per_op, key=lambda k: per_op[k]["ms"])
+    d = per_op[dom]
+    dom_w = C.get("3" if dom.startswith("space") else "4")
+    intensity = d["flop"] / d["min_bytes"]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": round(d["flop"] / d["ms"] / 1e9, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(d["min_bytes"] / d["ms"] / 1e6, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["traffic"] = read_traffic(dom)
+
+    out = {
+        "metric": "block-causal attention TFLOP/s (fwd, fwd+bwd) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Minecraft dynamics attention step: space layer fwd+bwd (B=4 x T=64 blocks "
+                        "of 290 tokens, 30 q / 3 kv heads, d 64, agent isolation) + time layer "
+                        "fwd+bwd (T=256 frames x 290 slots, causal, window 192)",
+            "space": {"B": ws.B, "T": ws.T, "N": ws.N, "Hq": ws.Hq, "Hkv": ws.Hkv, "D": ws.D,
+                      "agent_begin": ws.agent_begin, "agent_count": ws.agent_count},
+            "time": {"B": wt.B, "T": wt.T, "N": wt.N, "Hq": wt.Hq, "Hkv": wt.Hkv, "D": wt.D,
+                     "window": wt.window},
+            "flop_per_step": total_flops,
+        },
+        "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round((per_op["space_fwd"]["flop"] + per_op["time_fwd"]["flop"])
+                            / (per_op["space_fwd"]["ms"] + per_op["time_fwd"]["ms"]) / 1e9, 2),
+        "ops": {k: {kk: vv for kk, vv in v.items() if kk not in ("flop", "min_bytes")}
+                for k, v in per_op.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

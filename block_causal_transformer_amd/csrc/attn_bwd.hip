@@ -13,21 +13,27 @@
 //   dS = P o (dP - Delta),  dV = P^T dO,  dK = s dS^T Q,  dQ = s dS K,
 // with dK, dV of a KV head summed over the G query heads of its group.
 //
-// Decomposition.  One workgroup (4 waves) owns a whole (unit, KV head)
-// problem, so every sum stays inside it and no atomics are needed; the result
-// is bitwise deterministic.  Keys are cut into 16-key tiles dealt round-robin
-// to the waves; each wave keeps its tiles' K and V (as MFMA operands) and its
-// dK^T, dV^T accumulators in registers for the whole kernel.  The problem's
-// rows (position x head-in-group, as in the forward) are swept in 32-row
-// chunks:
-//   1. all threads stage Q, dO (row-major and transposed) and LSE of the
-//      chunk in LDS and compute Delta from O and dO on the fly (no separate
-//      pre-pass kernel, O is read exactly once);
-//   2. each wave, per own key tile: S and dP on MFMA, P and dS on VALU,
-//      dV^T += dO^T P and dK^T += Q^T dS on MFMA, and dS written to LDS;
-//   3. dQ^T = K^T dS^T for the chunk from LDS (K^T staged once), split over
-//      the waves by output tile, written straight to HBM.
-// Key tiles a chunk cannot see (causal and window ranges) are skipped.
+// Two kernels, each keeping one side of the problem stationary in registers
+// so that no sum crosses waves (no atomics; bitwise deterministic):
+//
+//  dq kernel  (query-parallel, laid out like the forward): a workgroup holds
+//             K, V and K^T of one (unit, KV head) problem in LDS; each wave
+//             owns 32 query rows (position x head-in-group) and sweeps the
+//             visible keys in 32-key steps: S^T = K Q^T and dP^T = V dO^T on
+//             MFMA (every lane holds one query column), P^T and dS^T on VALU,
+//             dQ^T += K^T dS^T on MFMA.  It also forms Delta from O and dO
+//             and leaves it in the workspace for the second kernel.
+//  dkv kernel (key-parallel): each wave owns 16-key tiles of one problem and
+//             keeps their dK^T, dV^T accumulators and K, V operands in
+//             registers; the problem's query rows stream through LDS in
+//             32-row chunks (double-buffered, prefetched into registers one
+//             chunk ahead): S = Q K^T and dP = dO V^T, then dV^T += dO^T P
+//             and dK^T += Q^T dS on MFMA.
+//
+// Key steps (dq) and query chunks (dkv) that the causal / window ranges make
+// invisible are never visited.  The split costs two more matmul passes than a
+// fused kernel (S and dP are formed in both) in exchange for half the
+// register footprint per wave, no LDS exchange of dS, and two waves per SIMD.
 #include "bca_device.h"
 #include "bca_kernels.h"
 
@@ -36,8 +42,6 @@ namespace bca {
 namespace {
 
 constexpr int KMAX = kMfmaBwdMaxLen;  // 320
-constexpr int QC = 32;                // rows per chunk
-constexpr int KTW = KMAX / 16 / 4;    // 16-key tiles per wave (5)
 
 struct BwdParams {
   const bf16* q;
@@ -49,18 +53,178 @@ struct BwdParams {
   bf16* dq;
   bf16* dk;
   bf16* dv;
-  int op, T, N, Hq, Hkv, G, L, units, rows;
+  float* delta;  // workspace, (B, T, N, Hq) fp32
+  int T, N, Hq, Hkv, G, L, units, rows;
   int window, agent_begin, agent_count;
   float scale, scale_log2;
+  int splits, rows_per_split;  // dq kernel
+  int nwg;                     // dkv kernel: workgroups per problem
 };
 
-__device__ __forceinline__ int kt_off(int d, int key) {  // sKT: [64][KMAX]
-  return d * KMAX + ((((key >> 3) ^ (d & 7))) << 3) + (key & 7);
+// ------------------------------------------------------------- dq kernel
+
+constexpr int DQ_W = 8;    // waves per workgroup
+constexpr int DQ_QC = 32;  // query rows per wave and chunk
+
+__device__ __forceinline__ int krow_off(int key, int chunk) {  // [KMAX][64], 16B chunks xor-swizzled
+  return key * 64 + ((chunk ^ (key & 7)) << 3);
 }
-__device__ __forceinline__ int ds_off(int q, int key) {  // sdS: [QC][KMAX]
-  return q * KMAX + ((((key >> 3) ^ (q & 7))) << 3) + (key & 7);
+// K^T is stored with keys permuted inside each group of 32 so that the 8 keys
+// a lane feeds to one MFMA are contiguous: key 32a + 16h + 4g + j sits at
+// position 32a + 8g + 4h + j.
+__device__ __forceinline__ int kperm(int key) {
+  return (key & ~31) | (((key >> 2) & 3) << 3) | (((key >> 4) & 1) << 2) | (key & 3);
 }
-__device__ __forceinline__ int row_off(int row, int chunk) {  // sQ, sdO: [QC][64]
+__device__ __forceinline__ int kt_off(int d, int pos) {  // [64][KMAX]
+  return d * KMAX + ((((pos >> 3) ^ (d & 7))) << 3) + (pos & 7);
+}
+
+struct DqSmem {
+  bf16 K[KMAX * 64];
+  bf16 V[KMAX * 64];
+  bf16 KT[64 * KMAX];
+};
+
+template <int OP>
+__global__ __attribute__((amdgpu_flat_work_group_size(DQ_W * 64, DQ_W * 64), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) DqSmem sm;
+  constexpr int NT = DQ_W * 64;
+
+  int ug, split;
+  xcd_remap(blockIdx.x, p.units * p.Hkv, p.splits, ug, split);
+  const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
+  const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, 64);
+  const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
+  const UnitGeom gl = unit_geom(OP, u, p.T, p.N, p.Hq, 1);
+  const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
+  const int G = p.G;
+  const int64_t qhead = (int64_t)g * G * 64;
+  const bf16* kbase = p.k + gk.base + g * 64;
+  const bf16* vbase = p.v + gk.base + g * 64;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int lp32 = (p.L + 31) & ~31;
+
+  for (int idx = tid; idx < lp32 * 8; idx += NT) {
+    const int r = idx >> 3, c = idx & 7;
+    const bool ok = r < p.L;
+    const bf16x8 kv = ok ? ld_global16(kbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
+    const bf16x8 vv = ok ? ld_global16(vbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
+    st_lds16(sm.K + krow_off(r, c), kv);
+    st_lds16(sm.V + krow_off(r, c), vv);
+    const int pp = kperm(r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm.KT[kt_off(c * 8 + e, pp)] = kv[e];
+  }
+  __syncthreads();
+
+  const int row0 = split * p.rows_per_split;
+  const int row1 = min(p.rows, row0 + p.rows_per_split);
+  const int nch = (row1 - row0 + DQ_QC - 1) / DQ_QC;
+
+  for (int ch = wave; ch < nch; ch += DQ_W) {
+    const int r0 = row0 + ch * DQ_QC;
+    // this lane's query column in each of the two 16-column tiles
+    bf16x8 qreg[2][2], dreg[2][2];
+    int qpos[2], hh[2];
+    bool qv[2];
+    float lse2[2], dlt[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int r = r0 + qt * 16 + li;
+      qv[qt] = r < row1;
+      const int rr = qv[qt] ? r : row0;
+      qpos[qt] = rr / G;
+      hh[qt] = rr - qpos[qt] * G;
+      const int64_t off = gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 8;
+      float part = 0.f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        qreg[qt][s] = qv[qt] ? ld_global16(p.q + off + s * 32) : zero8();
+        dreg[qt][s] = qv[qt] ? ld_global16(p.dout + off + s * 32) : zero8();
+        const bf16x8 ov = qv[qt] ? ld_global16(p.o + off + s * 32) : zero8();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += (float)dreg[qt][s][e] * (float)ov[e];
+      }
+      dlt[qt] = group4_sum(part);
+      const int64_t lo = gl.base + (int64_t)qpos[qt] * gl.pos_stride + g * G + hh[qt];
+      lse2[qt] = qv[qt] ? p.lse[lo] * kLog2e : INFINITY;
+      if (qv[qt] && lg == 0) p.delta[lo] = dlt[qt];
+    }
+    f32x4 acc[4][2];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      acc[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int qlo = r0 / G;
+    const int qhi = (min(r0 + DQ_QC, row1) - 1) / G;
+    int klo, khi;
+    key_range(md, qlo, qhi, klo, khi);
+    const int st0 = klo >> 5, st1 = (khi + 31) >> 5;
+    for (int st = st0; st < st1; ++st) {
+      const int kabs = st * 32;
+      f32x4 sc[2][2], dp[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = kabs + h * 16 + li;
+        const bf16x8 k0 = ld_lds16(sm.K + krow_off(kr, lg));
+        const bf16x8 k1 = ld_lds16(sm.K + krow_off(kr, 4 + lg));
+        const bf16x8 v0 = ld_lds16(sm.V + krow_off(kr, lg));
+        const bf16x8 v1 = ld_lds16(sm.V + krow_off(kr, 4 + lg));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          z = mfma16(k0, qreg[qt][0], z);
+          sc[qt][h] = mfma16(k1, qreg[qt][1], z);
+          f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          y = mfma16(v0, dreg[qt][0], y);
+          dp[qt][h] = mfma16(v1, dreg[qt][1], y);
+        }
+      }
+      const bool full = tile_all_visible(md, qlo, qhi, kabs, kabs + 32);
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        f32x4 d0, d1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool vis0 = full | visible_op<OP>(md, qpos[qt], kabs + lg * 4 + j);
+          const bool vis1 = full | visible_op<OP>(md, qpos[qt], kabs + 16 + lg * 4 + j);
+          const float e0 = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt]));
+          const float e1 = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt]));
+          d0[j] = vis0 ? e0 * (dp[qt][0][j] - dlt[qt]) : 0.f;
+          d1[j] = vis1 ? e1 * (dp[qt][1][j] - dlt[qt]) : 0.f;
+        }
+        dsb[qt] = pack8(d0, d1);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 kt = ld_lds16(sm.KT + kt_off(dt * 16 + li, kabs + lg * 8));
+        acc[dt][0] = mfma16(kt, dsb[0], acc[dt][0]);
+        acc[dt][1] = mfma16(kt, dsb[1], acc[dt][1]);
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      if (!qv[qt]) continue;
+      bf16* dst = p.dq + gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 4;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        *reinterpret_cast<u32x2*>(dst + dt * 16) = __builtin_bit_cast(u32x2, pack4(acc[dt][qt] * p.scale));
+    }
+  }
+}
+
+// ------------------------------------------------------------ dkv kernel
+
+constexpr int KV_W = 8;    // waves per workgroup
+constexpr int KV_TPW = 2;  // 16-key tiles per wave
+constexpr int KV_QC = 32;  // query rows per chunk
+
+__device__ __forceinline__ int row_off(int row, int chunk) {  // [32][64]
   return row * 64 + ((chunk ^ (row & 7)) << 3);
 }
 // Transposed chunk rows: query q of the chunk sits at position
@@ -69,26 +233,31 @@ __device__ __forceinline__ int row_off(int row, int chunk) {  // sQ, sdO: [QC][6
 __device__ __forceinline__ int tq_perm(int q) {
   return (((q >> 2) & 3) << 3) | ((q >> 4) << 2) | (q & 3);
 }
-__device__ __forceinline__ int tr_off(int d, int pos) {  // sQT, sdOT: [64][QC]
-  return d * QC + ((((pos >> 3) ^ (d & 3))) << 3) + (pos & 7);
+__device__ __forceinline__ int tr_off(int d, int pos) {  // [64][32]
+  return d * 32 + ((((pos >> 3) ^ (d & 3))) << 3) + (pos & 7);
 }
 
-__global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) bf16 sKT[64 * KMAX];
-  __shared__ __attribute__((aligned(16))) bf16 sdS[QC * KMAX];
-  __shared__ __attribute__((aligned(16))) bf16 sQ[QC * 64];
-  __shared__ __attribute__((aligned(16))) bf16 sdO[QC * 64];
-  __shared__ __attribute__((aligned(16))) bf16 sQT[64 * QC];
-  __shared__ __attribute__((aligned(16))) bf16 sdOT[64 * QC];
-  __shared__ __attribute__((aligned(16))) float sLse[QC];
-  __shared__ __attribute__((aligned(16))) float sDelta[QC];
+struct KvBuf {
+  bf16 Q[KV_QC * 64];
+  bf16 dO[KV_QC * 64];
+  bf16 QT[64 * KV_QC];
+  bf16 dOT[64 * KV_QC];
+  float lse[KV_QC];
+  float delta[KV_QC];
+};
 
-  const int ug = blockIdx.x;
+template <int OP>
+__global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) KvBuf buf[2];
+
+  int ug, wg;
+  xcd_remap(blockIdx.x, p.units * p.Hkv, p.nwg, ug, wg);
   const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
-  const UnitGeom gq = unit_geom(p.op, u, p.T, p.N, p.Hq, 64);
-  const UnitGeom gk = unit_geom(p.op, u, p.T, p.N, p.Hkv, 64);
-  const UnitGeom gl = unit_geom(p.op, u, p.T, p.N, p.Hq, 1);
-  const MaskDesc md{p.op, p.L, p.window, p.agent_begin, p.agent_count};
+  const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, 64);
+  const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
+  const UnitGeom gl = unit_geom(OP, u, p.T, p.N, p.Hq, 1);
+  const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
   const int G = p.G;
   const int64_t qhead = (int64_t)g * G * 64;
   const bf16* kbase = p.k + gk.base + g * 64;
@@ -97,28 +266,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int nkt = (p.L + 15) >> 4;
-  const int lp32 = (p.L + 31) & ~31;
 
-  // K^T of the problem in LDS (zero beyond L), for the dQ product.
-  for (int idx = tid; idx < lp32 * 8; idx += 256) {
-    const int r = idx >> 3, c = idx & 7;
-    const bf16x8 kv = r < p.L ? ld_global16(kbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
+  // Own tiles: tile = wg + nwg * (wave + KV_W * m); K and V as B operands.
+  int tile[KV_TPW];
+  bool town[KV_TPW];
+  bf16x8 KB[KV_TPW][2], VB[KV_TPW][2];
+  f32x4 dKT[KV_TPW][4], dVT[KV_TPW][4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sKT[kt_off(c * 8 + e, r)] = kv[e];
-  }
-  // dS columns of the padding tile (never written by the waves) stay zero.
-  for (int idx = tid; idx < QC * (lp32 - nkt * 16); idx += 256) {
-    const int qrow = idx / (lp32 - nkt * 16), col = nkt * 16 + idx % (lp32 - nkt * 16);
-    sdS[ds_off(qrow, col)] = (bf16)0.f;
-  }
-
-  // Own key tiles: kt = wave + 4*m.  K and V as B operands (column = key).
-  bf16x8 KB[KTW][2], VB[KTW][2];
-  f32x4 dKT[KTW][4], dVT[KTW][4];
-#pragma unroll
-  for (int m = 0; m < KTW; ++m) {
-    const int key = (wave + 4 * m) * 16 + li;
-    const bool ok = key < p.L;
+  for (int m = 0; m < KV_TPW; ++m) {
+    tile[m] = wg + p.nwg * (wave + KV_W * m);
+    town[m] = tile[m] < nkt;
+    const int key = tile[m] * 16 + li;
+    const bool ok = town[m] && key < p.L;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       KB[m][s] = ok ? ld_global16(kbase + (int64_t)key * gk.pos_stride + s * 32 + lg * 8) : zero8();
@@ -130,87 +289,96 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
       dVT[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-
-  const int nchunks = (p.rows + QC - 1) / QC;
-  for (int c = 0; c < nchunks; ++c) {
-    const int r0 = c * QC;
-    // ---- 1. stage the chunk (one 16-byte piece of Q, dO, O per thread)
-    {
-      const int row = tid >> 3, ch = tid & 7;
-      const int r = r0 + row;
-      const bool valid = r < p.rows;
-      const int pos = valid ? r / G : 0;
-      const int hh = valid ? r - pos * G : 0;
-      const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + ch * 8;
-      const bf16x8 qv = valid ? ld_global16(p.q + off) : zero8();
-      const bf16x8 dov = valid ? ld_global16(p.dout + off) : zero8();
-      const bf16x8 ov = valid ? ld_global16(p.o + off) : zero8();
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part += (float)dov[e] * (float)ov[e];
-      part += __shfl_xor(part, 1);
-      part += __shfl_xor(part, 2);
-      part += __shfl_xor(part, 4);
-      st_lds16(sQ + row_off(row, ch), qv);
-      st_lds16(sdO + row_off(row, ch), dov);
-      const int tp = tq_perm(row);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sQT[tr_off(ch * 8 + e, tp)] = qv[e];
-        sdOT[tr_off(ch * 8 + e, tp)] = dov[e];
-      }
-      if (ch == 0) {
-        sDelta[row] = part;
-        sLse[row] = valid ? p.lse[gl.base + (int64_t)pos * gl.pos_stride + g * G + hh] * kLog2e
-                          : INFINITY;
+  // key range of the whole workgroup, for skipping query chunks
+  int kmin = p.L, kmax = -1;
+  for (int m = 0; m < KV_TPW; ++m)
+    for (int w = 0; w < KV_W; ++w) {
+      const int t = wg + p.nwg * (w + KV_W * m);
+      if (t < nkt) {
+        kmin = min(kmin, t * 16);
+        kmax = max(kmax, min(p.L, t * 16 + 16) - 1);
       }
     }
-    __syncthreads();
+  // query positions that can see any of those keys
+  int qpos_lo = 0, qpos_hi = p.L - 1;
+  if (OP == OP_TIME) {
+    qpos_lo = kmin;
+    qpos_hi = p.window > 0 ? min(p.L - 1, kmax + p.window - 1) : p.L - 1;
+  }
+  const int c_begin = kmax < 0 ? 0 : (qpos_lo * G) / KV_QC;
+  const int c_end = kmax < 0 ? 0 : ((qpos_hi + 1) * G + KV_QC - 1) / KV_QC;
 
-    // ---- 2. per-wave key tiles
+  // staging: threads 0..255 carry Q (and LSE), threads 256..511 dO (and Delta);
+  // a piece is (row, 16-byte column chunk) of the chunk
+  const bool carries_q = tid < 256;
+  const int srow = (tid & 255) >> 3, sch = tid & 7;
+  bf16x8 pre = zero8();
+  float pre_s = 0.f;
+  auto fetch = [&](int c) {
+    const int r = c * KV_QC + srow;
+    const bool valid = r < p.rows;
+    const int pos = valid ? r / G : 0;
+    const int hh = valid ? r - pos * G : 0;
+    const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + sch * 8;
+    const int64_t lo = gl.base + (int64_t)pos * gl.pos_stride + g * G + hh;
+    if (carries_q) {
+      pre = valid ? ld_global16(p.q + off) : zero8();
+      pre_s = valid ? p.lse[lo] * kLog2e : INFINITY;
+    } else {
+      pre = valid ? ld_global16(p.dout + off) : zero8();
+      pre_s = valid ? p.delta[lo] : 0.f;
+    }
+  };
+  auto stage = [&](KvBuf& b) {
+    const int tp = tq_perm(srow);
+    bf16* rowm = carries_q ? b.Q : b.dO;
+    bf16* trm = carries_q ? b.QT : b.dOT;
+    st_lds16(rowm + row_off(srow, sch), pre);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) trm[tr_off(sch * 8 + e, tp)] = pre[e];
+    if (sch == 0) (carries_q ? b.lse : b.delta)[srow] = pre_s;
+  };
+
+  if (c_begin < c_end) {
+    fetch(c_begin);
+    stage(buf[0]);
+    if (c_begin + 1 < c_end) fetch(c_begin + 1);
+  }
+  __syncthreads();
+
+  for (int c = c_begin; c < c_end; ++c) {
+    KvBuf& b = buf[(c - c_begin) & 1];
+    const int r0 = c * KV_QC;
     const int qlo = r0 / G;
-    const int qhi = (min(r0 + QC, p.rows) - 1) / G;
-    int klo, khi;
-    key_range(md, qlo, qhi, klo, khi);
-    const int step_lo = klo >> 5, step_hi = (khi + 31) >> 5;  // dQ key steps
-    {
-      bf16x8 Qa[2][2], dOa[2][2], QTa[4], dOTa[4];
+    const int qhi = (min(r0 + KV_QC, p.rows) - 1) / G;
+    // chunk operands: Q, dO rows (A of S, dP) and Q^T, dO^T (A of dK^T, dV^T)
+    bf16x8 Qa[2][2], dOa[2][2], QTa[4], dOTa[4];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          Qa[qt][s] = ld_lds16(sQ + row_off(qt * 16 + li, s * 4 + lg));
-          dOa[qt][s] = ld_lds16(sdO + row_off(qt * 16 + li, s * 4 + lg));
-        }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        QTa[dt] = ld_lds16(sQT + tr_off(dt * 16 + li, lg * 8));
-        dOTa[dt] = ld_lds16(sdOT + tr_off(dt * 16 + li, lg * 8));
+      for (int s = 0; s < 2; ++s) {
+        Qa[qt][s] = ld_lds16(b.Q + row_off(qt * 16 + li, s * 4 + lg));
+        dOa[qt][s] = ld_lds16(b.dO + row_off(qt * 16 + li, s * 4 + lg));
       }
-      f32x4 lse4[2], dl4[2];
-      int qpr[2][4];
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        lse4[qt] = *reinterpret_cast<const f32x4*>(sLse + qt * 16 + lg * 4);
-        dl4[qt] = *reinterpret_cast<const f32x4*>(sDelta + qt * 16 + lg * 4);
+    for (int dt = 0; dt < 4; ++dt) {
+      QTa[dt] = ld_lds16(b.QT + tr_off(dt * 16 + li, lg * 8));
+      dOTa[dt] = ld_lds16(b.dOT + tr_off(dt * 16 + li, lg * 8));
+    }
+    f32x4 lse4[2], dl4[2];
+    int qp[2][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qpr[qt][j] = (r0 + qt * 16 + lg * 4 + j) / G;
-      }
-
+    for (int qt = 0; qt < 2; ++qt) {
+      lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
+      dl4[qt] = *reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
 #pragma unroll
-      for (int m = 0; m < KTW; ++m) {
-        const int kt = wave + 4 * m;
-        if (kt >= nkt) break;
-        const int kabs = kt * 16;
-        if (kabs + 16 <= klo || kabs >= khi || tile_none_visible(md, qlo, qhi, kabs, kabs + 16)) {
-          if (kabs < step_hi * 32 && kabs + 16 > step_lo * 32) {
+      for (int j = 0; j < 4; ++j) qp[qt][j] = (r0 + qt * 16 + lg * 4 + j) / G;
+    }
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) sdS[ds_off(qt * 16 + lg * 4 + j, kabs + li)] = (bf16)0.f;
-          }
-          continue;
-        }
+    for (int m = 0; m < KV_TPW; ++m) {
+      const int kabs = tile[m] * 16;
+      const bool work = town[m] && !tile_none_visible(md, qlo, qhi, kabs, kabs + 16);
+      if (work) {
         f32x4 S[2], dP[2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
@@ -227,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
         for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bool vis = full || visible(md, qpr[qt][j], kabs + li);
+            const bool vis = full | visible_op<OP>(md, qp[qt][j], kabs + li);
             const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
             const float pv = vis ? e : 0.f;
             P[qt][j] = pv;
@@ -240,44 +408,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
           dVT[m][dt] = mfma16(dOTa[dt], Pb, dVT[m][dt]);
           dKT[m][dt] = mfma16(QTa[dt], dSb, dKT[m][dt]);
         }
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) sdS[ds_off(qt * 16 + lg * 4 + j, kabs + li)] = dSb[qt * 4 + j];
       }
+    }
+    // next chunk into the other buffer (last read before the previous
+    // barrier), then prefetch the one after
+    if (c + 1 < c_end) {
+      stage(buf[(c + 1 - c_begin) & 1]);
+      if (c + 2 < c_end) fetch(c + 2);
     }
     __syncthreads();
-
-    // ---- 3. dQ^T = K^T dS^T: wave w computes query tile (w & 1) for the two
-    // 16-wide head-dim tiles 2*(w >> 1) and 2*(w >> 1) + 1.
-    {
-      const int qt = wave & 1, dt0 = (wave >> 1) * 2;
-      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-      for (int st = step_lo; st < step_hi; ++st) {
-        const bf16x8 b = ld_lds16(sdS + ds_off(qt * 16 + li, st * 32 + lg * 8));
-        const bf16x8 k0 = ld_lds16(sKT + kt_off(dt0 * 16 + li, st * 32 + lg * 8));
-        const bf16x8 k1 = ld_lds16(sKT + kt_off(dt0 * 16 + 16 + li, st * 32 + lg * 8));
-        a0 = mfma16(k0, b, a0);
-        a1 = mfma16(k1, b, a1);
-      }
-      const int r = r0 + qt * 16 + li;
-      if (r < p.rows) {
-        const int pos = r / G, hh = r - (r / G) * G;
-        bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + lg * 4;
-        *reinterpret_cast<u32x2*>(dst + dt0 * 16) = __builtin_bit_cast(u32x2, pack4(a0 * p.scale));
-        *reinterpret_cast<u32x2*>(dst + dt0 * 16 + 16) = __builtin_bit_cast(u32x2, pack4(a1 * p.scale));
-      }
-    }
-    // The next chunk's staging writes sQ/sdO/sQT/sdOT/sLse/sDelta only,
-    // which no wave reads after the barrier above; its barrier then orders
-    // these dS reads before the next chunk's dS writes.
   }
 
-  // ---- dK, dV of the own tiles: lane holds column key, rows d = dt*16 + lg*4 + j
 #pragma unroll
-  for (int m = 0; m < KTW; ++m) {
-    const int key = (wave + 4 * m) * 16 + li;
-    if (key >= p.L) continue;
+  for (int m = 0; m < KV_TPW; ++m) {
+    const int key = tile[m] * 16 + li;
+    if (!town[m] || key >= p.L) continue;
     bf16* dkd = p.dk + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
     bf16* dvd = p.dv + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
 #pragma unroll
@@ -290,9 +435,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kernel(BwdParams p) {
 
 }  // namespace
 
+size_t bwd_bf16_workspace_bytes(const AttnDims& d) {
+  return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
+}
+
 hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k, const void* v,
                                 const void* o, const float* lse, const void* dout, void* dq,
-                                void* dk, void* dv, hipStream_t stream) {
+                                void* dk, void* dv, void* workspace, hipStream_t stream) {
   BwdParams p;
   p.q = static_cast<const bf16*>(q);
   p.k = static_cast<const bf16*>(k);
@@ -303,7 +452,7 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.dq = static_cast<bf16*>(dq);
   p.dk = static_cast<bf16*>(dk);
   p.dv = static_cast<bf16*>(dv);
-  p.op = d.op;
+  p.delta = static_cast<float*>(workspace);
   p.T = d.T;
   p.N = d.N;
   p.Hq = d.Hq;
@@ -318,9 +467,31 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.scale = d.scale;
   p.scale_log2 = d.scale * kLog2e;
   if (p.L > KMAX) return hipErrorInvalidValue;
-  const long grid = (long)p.units * p.Hkv;
-  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_bwd_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  const long problems = (long)p.units * p.Hkv;
+
+  // dq kernel: one workgroup per CU (LDS), rows split so the grid covers the
+  // CUs a few times over
+  const int chunks = (p.rows + DQ_QC - 1) / DQ_QC;
+  int splits = (int)((3 * 256 + problems - 1) / problems);
+  splits = max(1, min(splits, (chunks + DQ_W - 1) / DQ_W));
+  int per = (chunks + splits - 1) / splits;
+  per = ((per + DQ_W - 1) / DQ_W) * DQ_W;
+  p.rows_per_split = per * DQ_QC;
+  p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
+  const long g1 = problems * p.splits;
+  // dkv kernel: enough workgroups per problem to give every wave its tiles
+  const int nkt = (p.L + 15) / 16;
+  p.nwg = max(1, (nkt + KV_W * KV_TPW - 1) / (KV_W * KV_TPW));
+  const long g2 = problems * p.nwg;
+  if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
+
+  if (d.op == OP_SPACE) {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<OP_SPACE>, dim3((unsigned)g2), dim3(KV_W * 64), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<OP_TIME>, dim3((unsigned)g2), dim3(KV_W * 64), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

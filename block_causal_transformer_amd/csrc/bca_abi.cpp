@@ -83,7 +83,7 @@ int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
 }
 
 size_t workspace_bytes(const bca::AttnDims& d) {
-  if (bca::bwd_uses_mfma(d)) return 0;
+  if (bca::bwd_uses_mfma(d)) return bca::bwd_bf16_workspace_bytes(d);
   return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
 }
 
@@ -129,7 +129,7 @@ int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = bca::bwd_uses_mfma(d)
-                     ? bca::launch_attn_bwd_bf16(d, q, k, v, o, lse, dout, dq, dk, dv, s)
+                     ? bca::launch_attn_bwd_bf16(d, q, k, v, o, lse, dout, dq, dk, dv, workspace, s)
                      : bca::launch_attn_bwd_generic(d, q, k, v, o, lse, dout, dq, dk, dv,
                                                     static_cast<float*>(workspace), s);
   st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_bwd launch" : "time_attn_bwd launch");

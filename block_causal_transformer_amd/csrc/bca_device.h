@@ -123,6 +123,18 @@ __device__ __forceinline__ bool visible(const MaskDesc& m, int qp, int kp) {
   return !(ka && !qa);
 }
 
+// Branch-free form of visible() for a mask kind fixed at compile time.
+template <int OP>
+__device__ __forceinline__ bool visible_op(const MaskDesc& m, int qp, int kp) {
+  if constexpr (OP == OP_TIME) {
+    return (kp <= qp) & (kp < m.L) & ((m.window == 0) | (qp - kp < m.window));
+  } else {
+    const bool ka = (unsigned)(kp - m.agent_begin) < (unsigned)m.agent_count;
+    const bool qa = (unsigned)(qp - m.agent_begin) < (unsigned)m.agent_count;
+    return (kp < m.L) & !(ka & !qa);
+  }
+}
+
 // Key-position range [lo, hi) that any query position in [qlo, qhi] can see.
 __device__ __forceinline__ void key_range(const MaskDesc& m, int qlo, int qhi, int& lo, int& hi) {
   if (m.op == OP_TIME) {

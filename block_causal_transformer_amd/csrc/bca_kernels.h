@@ -25,7 +25,10 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
                                 void* o, float* lse, hipStream_t stream);
 hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k, const void* v,
                                 const void* o, const float* lse, const void* dout, void* dq,
-                                void* dk, void* dv, hipStream_t stream);
+                                void* dk, void* dv, void* workspace, hipStream_t stream);
+// Workspace of the MFMA backward: the fp32 Delta = rowsum(dO * O) per
+// (query, head), written by its first kernel and read by its second.
+size_t bwd_bf16_workspace_bytes(const AttnDims& d);
 
 // Generic VALU kernels: fp32 or bf16 storage, D = 32 or 64, any length.
 hipError_t launch_attn_fwd_generic(const AttnDims& d, const void* q, const void* k,

@@ -128,9 +128,9 @@ int time_attn_bwd(const bca_shape* shape, const bca_mask* mask, const void* q,
                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace the backward of `op` needs for `shape` (0 when
- * the LDS-resident MFMA backward runs; the fp32 Delta = rowsum(dO * O) buffer
- * otherwise).  Returns 0 for an invalid shape. */
+/* Bytes of device workspace the backward of `op` needs for `shape`: one fp32
+ * Delta = rowsum(dO * O) per (query, head), i.e. B*T*N*Hq*4 bytes.  Returns 0
+ * for an invalid shape. */
 size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape);
 
 /* Static string naming a status code. */

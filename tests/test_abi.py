@@ -124,10 +124,9 @@ def test_mask_descriptor_rules(lib):
 
 
 def test_workspace_query_and_check(lib):
-    # LDS-resident MFMA backward (bf16, D 64, <= 320 positions): no workspace
-    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=290)) == 0
-    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=256)) == 0
-    # generic backward: one fp32 Delta per (query, head)
+    # every backward path: one fp32 Delta per (query, head)
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=290)) == 1 * 4 * 290 * 4 * 4
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=256)) == 1 * 256 * 10 * 4 * 4
     s = good_shape(N=1432, T=2)
     need = ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, s)
     assert need == 1 * 2 * 1432 * 4 * 4
