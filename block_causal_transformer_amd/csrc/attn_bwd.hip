@@ -56,7 +56,7 @@ struct BwdParams {
   float* delta;  // workspace, (B, T, N, Hq) fp32
   int T, N, Hq, Hkv, G, L, units, rows;
   int window, agent_begin, agent_count;
-  float scale, scale_log2;
+  float scale, scale_log2, inv_g;
   int splits, rows_per_split;  // dq kernel
   int nwg;                     // dkv kernel: workgroups per problem
 };
@@ -126,7 +126,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
   for (int ch = wave; ch < nch; ch += DQ_W) {
     const int r0 = row0 + ch * DQ_QC;
-    // this lane's query column in each of the two 16-column tiles
+    // this lane's query column in each of the two 16-column tiles; padding
+    // columns read a real row (clamped) and are never stored
     bf16x8 qreg[2][2], dreg[2][2];
     int qpos[2], hh[2];
     bool qv[2];
@@ -135,22 +136,23 @@ void attn_bwd_dq_kernel(BwdParams p) {
     for (int qt = 0; qt < 2; ++qt) {
       const int r = r0 + qt * 16 + li;
       qv[qt] = r < row1;
-      const int rr = qv[qt] ? r : row0;
-      qpos[qt] = rr / G;
+      const int rr = min(r, row1 - 1);
+      qpos[qt] = row_pos(rr, p.inv_g);
       hh[qt] = rr - qpos[qt] * G;
       const int64_t off = gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 8;
       float part = 0.f;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        qreg[qt][s] = qv[qt] ? ld_global16(p.q + off + s * 32) : zero8();
-        dreg[qt][s] = qv[qt] ? ld_global16(p.dout + off + s * 32) : zero8();
-        const bf16x8 ov = qv[qt] ? ld_global16(p.o + off + s * 32) : zero8();
+        qreg[qt][s] = ld_global16(p.q + off + s * 32);
+        dreg[qt][s] = ld_global16(p.dout + off + s * 32);
+        const bf16x8 ov = ld_global16(p.o + off + s * 32);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part += (float)dreg[qt][s][e] * (float)ov[e];
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)dreg[qt][s][e], (float)ov[e], part);
       }
       dlt[qt] = group4_sum(part);
       const int64_t lo = gl.base + (int64_t)qpos[qt] * gl.pos_stride + g * G + hh[qt];
-      lse2[qt] = qv[qt] ? p.lse[lo] * kLog2e : INFINITY;
+      const float l = p.lse[lo];
+      lse2[qt] = qv[qt] ? l * kLog2e : INFINITY;
       if (qv[qt] && lg == 0) p.delta[lo] = dlt[qt];
     }
     f32x4 acc[4][2];
@@ -179,26 +181,39 @@ void attn_bwd_dq_kernel(BwdParams p) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
           z = mfma16(k0, qreg[qt][0], z);
           sc[qt][h] = mfma16(k1, qreg[qt][1], z);
-          f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          // the accumulator starts at -Delta, so it ends at dP - Delta
+          f32x4 y = {-dlt[qt], -dlt[qt], -dlt[qt], -dlt[qt]};
           y = mfma16(v0, dreg[qt][0], y);
           dp[qt][h] = mfma16(v1, dreg[qt][1], y);
         }
       }
-      const bool full = tile_all_visible(md, qlo, qhi, kabs, kabs + 32);
       bf16x8 dsb[2];
+      if (tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        f32x4 d0, d1;
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4 d0, d1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool vis0 = full | visible_op<OP>(md, qpos[qt], kabs + lg * 4 + j);
-          const bool vis1 = full | visible_op<OP>(md, qpos[qt], kabs + 16 + lg * 4 + j);
-          const float e0 = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt]));
-          const float e1 = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt]));
-          d0[j] = vis0 ? e0 * (dp[qt][0][j] - dlt[qt]) : 0.f;
-          d1[j] = vis1 ? e1 * (dp[qt][1][j] - dlt[qt]) : 0.f;
+          for (int j = 0; j < 4; ++j) {
+            d0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt])) * dp[qt][0][j];
+            d1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt])) * dp[qt][1][j];
+          }
+          dsb[qt] = pack8(d0, d1);
         }
-        dsb[qt] = pack8(d0, d1);
+      } else {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x4 d0, d1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool vis0 = visible_op<OP>(md, qpos[qt], kabs + lg * 4 + j);
+            const bool vis1 = visible_op<OP>(md, qpos[qt], kabs + 16 + lg * 4 + j);
+            const float e0 = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt])) * dp[qt][0][j];
+            const float e1 = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt])) * dp[qt][1][j];
+            d0[j] = vis0 ? e0 : 0.f;
+            d1[j] = vis1 ? e1 : 0.f;
+          }
+          dsb[qt] = pack8(d0, d1);
+        }
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -315,18 +330,21 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   bf16x8 pre = zero8();
   float pre_s = 0.f;
   auto fetch = [&](int c) {
+    // padding rows read a real (clamped) row; their LSE of +inf zeroes P
     const int r = c * KV_QC + srow;
     const bool valid = r < p.rows;
-    const int pos = valid ? r / G : 0;
-    const int hh = valid ? r - pos * G : 0;
+    const int rr = min(r, p.rows - 1);
+    const int pos = row_pos(rr, p.inv_g);
+    const int hh = rr - pos * G;
     const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + sch * 8;
     const int64_t lo = gl.base + (int64_t)pos * gl.pos_stride + g * G + hh;
     if (carries_q) {
-      pre = valid ? ld_global16(p.q + off) : zero8();
-      pre_s = valid ? p.lse[lo] * kLog2e : INFINITY;
+      pre = ld_global16(p.q + off);
+      const float l = p.lse[lo];
+      pre_s = valid ? l * kLog2e : INFINITY;
     } else {
-      pre = valid ? ld_global16(p.dout + off) : zero8();
-      pre_s = valid ? p.delta[lo] : 0.f;
+      pre = ld_global16(p.dout + off);
+      pre_s = p.delta[lo];
     }
   };
   auto stage = [&](KvBuf& b) {
@@ -365,14 +383,11 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       QTa[dt] = ld_lds16(b.QT + tr_off(dt * 16 + li, lg * 8));
       dOTa[dt] = ld_lds16(b.dOT + tr_off(dt * 16 + li, lg * 8));
     }
-    f32x4 lse4[2], dl4[2];
-    int qp[2][4];
+    f32x4 lse4[2], ndl4[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
-      dl4[qt] = *reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) qp[qt][j] = (r0 + qt * 16 + lg * 4 + j) / G;
+      ndl4[qt] = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
     }
 #pragma unroll
     for (int m = 0; m < KV_TPW; ++m) {
@@ -385,22 +400,34 @@ void attn_bwd_dkv_kernel(BwdParams p) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
           z = mfma16(Qa[qt][0], KB[m][0], z);
           S[qt] = mfma16(Qa[qt][1], KB[m][1], z);
-          f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          // the accumulator starts at -Delta, so it ends at dP - Delta
+          f32x4 y = ndl4[qt];
           y = mfma16(dOa[qt][0], VB[m][0], y);
           dP[qt] = mfma16(dOa[qt][1], VB[m][1], y);
         }
-        const bool full = tile_all_visible(md, qlo, qhi, kabs, kabs + 16);
         f32x4 P[2], dS[2];
+        if (tile_all_visible(md, qlo, qhi, kabs, kabs + 16)) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+          for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bool vis = full | visible_op<OP>(md, qp[qt][j], kabs + li);
-            const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
-            const float pv = vis ? e : 0.f;
-            P[qt][j] = pv;
-            dS[qt][j] = pv * (dP[qt][j] - dl4[qt][j]);
-          }
+            for (int j = 0; j < 4; ++j) {
+              const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
+              P[qt][j] = e;
+              dS[qt][j] = e * dP[qt][j];
+            }
+        } else {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int qp = row_pos(r0 + qt * 16 + lg * 4 + j, p.inv_g);
+              const bool vis = visible_op<OP>(md, qp, kabs + li);
+              const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
+              const float pv = vis ? e : 0.f;
+              P[qt][j] = pv;
+              dS[qt][j] = pv * dP[qt][j];
+            }
+        }
         const bf16x8 Pb = pack8(P[0], P[1]);
         const bf16x8 dSb = pack8(dS[0], dS[1]);
 #pragma unroll
@@ -466,7 +493,8 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.agent_count = d.agent_count;
   p.scale = d.scale;
   p.scale_log2 = d.scale * kLog2e;
-  if (p.L > KMAX) return hipErrorInvalidValue;
+  p.inv_g = 1.0f / (float)p.G;
+  if (p.L > KMAX || p.G > 256) return hipErrorInvalidValue;
   const long problems = (long)p.units * p.Hkv;
 
   // dq kernel: one workgroup per CU (LDS), rows split so the grid covers the

@@ -135,6 +135,13 @@ __device__ __forceinline__ bool visible_op(const MaskDesc& m, int qp, int kp) {
   }
 }
 
+// Position (row / G) of a folded row index, exact for rows < 2^21 and
+// G <= 256: (r + 0.5) / G keeps a margin of 0.5/G from the next integer,
+// more than the two fp32 roundings can move it.
+__device__ __forceinline__ int row_pos(int r, float inv_g) {
+  return (int)(((float)r + 0.5f) * inv_g);
+}
+
 // Key-position range [lo, hi) that any query position in [qlo, qhi] can see.
 __device__ __forceinline__ void key_range(const MaskDesc& m, int qlo, int qhi, int& lo, int& hi) {
   if (m.op == OP_TIME) {
