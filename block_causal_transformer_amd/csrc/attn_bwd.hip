@@ -58,7 +58,7 @@ struct BwdParams {
   int window, agent_begin, agent_count;
   float scale, scale_log2, inv_g;
   int splits, rows_per_split;  // dq kernel
-  int nwg;                     // dkv kernel: workgroups per problem
+  int nwg;                     // dkv kernel: workgroups per problem (1)
 };
 
 // ------------------------------------------------------------- dq kernel
@@ -236,7 +236,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------ dkv kernel
 
 constexpr int KV_W = 8;    // waves per workgroup
-constexpr int KV_TPW = 2;  // 16-key tiles per wave
+constexpr int KV_TPW = 3;  // 16-key tile slots per wave (tile = wave + 8 * slot)
 constexpr int KV_QC = 32;  // query rows per chunk
 
 __device__ __forceinline__ int row_off(int row, int chunk) {  // [32][64]
@@ -261,13 +261,23 @@ struct KvBuf {
   float delta[KV_QC];
 };
 
+struct KvSmem {
+  bf16 K[KMAX * 64];  // rows of the problem's keys (B operands of S)
+  bf16 V[KMAX * 64];  // (B operands of dP)
+  KvBuf buf[2];
+};
+
+// One workgroup per (unit, KV head) problem.  The two waves of a SIMD (w and
+// w + 4) hold 5 of the 20 tile slots between them, so the SIMDs stay within
+// one tile of each other even though the waves do not.
 template <int OP>
 __global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) KvBuf buf[2];
+  __shared__ __attribute__((aligned(16))) KvSmem sm;
+  constexpr int NT = KV_W * 64;
 
   int ug, wg;
-  xcd_remap(blockIdx.x, p.units * p.Hkv, p.nwg, ug, wg);
+  xcd_remap(blockIdx.x, p.units * p.Hkv, 1, ug, wg);
   const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
   const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, 64);
   const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
@@ -281,47 +291,25 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   const int nkt = (p.L + 15) >> 4;
+  const int lp16 = nkt * 16;
 
-  // Own tiles: tile = wg + nwg * (wave + KV_W * m); K and V as B operands.
-  int tile[KV_TPW];
-  bool town[KV_TPW];
-  bf16x8 KB[KV_TPW][2], VB[KV_TPW][2];
+  for (int idx = tid; idx < lp16 * 8; idx += NT) {
+    const int r = idx >> 3, c = idx & 7;
+    const bool ok = r < p.L;
+    const bf16x8 kv = ok ? ld_global16(kbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
+    const bf16x8 vv = ok ? ld_global16(vbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
+    st_lds16(sm.K + krow_off(r, c), kv);
+    st_lds16(sm.V + krow_off(r, c), vv);
+  }
+
   f32x4 dKT[KV_TPW][4], dVT[KV_TPW][4];
 #pragma unroll
-  for (int m = 0; m < KV_TPW; ++m) {
-    tile[m] = wg + p.nwg * (wave + KV_W * m);
-    town[m] = tile[m] < nkt;
-    const int key = tile[m] * 16 + li;
-    const bool ok = town[m] && key < p.L;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      KB[m][s] = ok ? ld_global16(kbase + (int64_t)key * gk.pos_stride + s * 32 + lg * 8) : zero8();
-      VB[m][s] = ok ? ld_global16(vbase + (int64_t)key * gk.pos_stride + s * 32 + lg * 8) : zero8();
-    }
+  for (int m = 0; m < KV_TPW; ++m)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       dKT[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       dVT[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  }
-  // key range of the whole workgroup, for skipping query chunks
-  int kmin = p.L, kmax = -1;
-  for (int m = 0; m < KV_TPW; ++m)
-    for (int w = 0; w < KV_W; ++w) {
-      const int t = wg + p.nwg * (w + KV_W * m);
-      if (t < nkt) {
-        kmin = min(kmin, t * 16);
-        kmax = max(kmax, min(p.L, t * 16 + 16) - 1);
-      }
-    }
-  // query positions that can see any of those keys
-  int qpos_lo = 0, qpos_hi = p.L - 1;
-  if (OP == OP_TIME) {
-    qpos_lo = kmin;
-    qpos_hi = p.window > 0 ? min(p.L - 1, kmax + p.window - 1) : p.L - 1;
-  }
-  const int c_begin = kmax < 0 ? 0 : (qpos_lo * G) / KV_QC;
-  const int c_end = kmax < 0 ? 0 : ((qpos_hi + 1) * G + KV_QC - 1) / KV_QC;
 
   // staging: threads 0..255 carry Q (and LSE), threads 256..511 dO (and Delta);
   // a piece is (row, 16-byte column chunk) of the chunk
@@ -357,99 +345,117 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     if (sch == 0) (carries_q ? b.lse : b.delta)[srow] = pre_s;
   };
 
-  if (c_begin < c_end) {
-    fetch(c_begin);
-    stage(buf[0]);
-    if (c_begin + 1 < c_end) fetch(c_begin + 1);
-  }
+  const int nchunks = (p.rows + KV_QC - 1) / KV_QC;
+  fetch(0);
+  stage(sm.buf[0]);
+  if (1 < nchunks) fetch(1);
   __syncthreads();
 
-  for (int c = c_begin; c < c_end; ++c) {
-    KvBuf& b = buf[(c - c_begin) & 1];
+  for (int c = 0; c < nchunks; ++c) {
+    KvBuf& b = sm.buf[c & 1];
     const int r0 = c * KV_QC;
     const int qlo = r0 / G;
     const int qhi = (min(r0 + KV_QC, p.rows) - 1) / G;
-    // chunk operands: Q, dO rows (A of S, dP) and Q^T, dO^T (A of dK^T, dV^T)
-    bf16x8 Qa[2][2], dOa[2][2], QTa[4], dOTa[4];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        Qa[qt][s] = ld_lds16(b.Q + row_off(qt * 16 + li, s * 4 + lg));
-        dOa[qt][s] = ld_lds16(b.dO + row_off(qt * 16 + li, s * 4 + lg));
-      }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      QTa[dt] = ld_lds16(b.QT + tr_off(dt * 16 + li, lg * 8));
-      dOTa[dt] = ld_lds16(b.dOT + tr_off(dt * 16 + li, lg * 8));
-    }
-    f32x4 lse4[2], ndl4[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
-      ndl4[qt] = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
-    }
+    bool work[KV_TPW];
+    bool anyw = false;
 #pragma unroll
     for (int m = 0; m < KV_TPW; ++m) {
-      const int kabs = tile[m] * 16;
-      const bool work = town[m] && !tile_none_visible(md, qlo, qhi, kabs, kabs + 16);
-      if (work) {
-        f32x4 S[2], dP[2];
+      const int t = wave + KV_W * m;
+      work[m] = t < nkt && !tile_none_visible(md, qlo, qhi, t * 16, t * 16 + 16);
+      anyw |= work[m];
+    }
+    if (anyw) {
+      // 1. S and dP for the owned tiles, then P and dS as packed B operands
+      bf16x8 Pb[KV_TPW], dSb[KV_TPW];
+      {
+        bf16x8 Qa[2][2], dOa[2][2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            Qa[qt][s] = ld_lds16(b.Q + row_off(qt * 16 + li, s * 4 + lg));
+            dOa[qt][s] = ld_lds16(b.dO + row_off(qt * 16 + li, s * 4 + lg));
+          }
+        f32x4 lse4[2], ndl4[2];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = mfma16(Qa[qt][0], KB[m][0], z);
-          S[qt] = mfma16(Qa[qt][1], KB[m][1], z);
-          // the accumulator starts at -Delta, so it ends at dP - Delta
-          f32x4 y = ndl4[qt];
-          y = mfma16(dOa[qt][0], VB[m][0], y);
-          dP[qt] = mfma16(dOa[qt][1], VB[m][1], y);
+          lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
+          ndl4[qt] = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
         }
-        f32x4 P[2], dS[2];
-        if (tile_all_visible(md, qlo, qhi, kabs, kabs + 16)) {
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
+        for (int m = 0; m < KV_TPW; ++m) {
+          if (!work[m]) continue;
+          const int kabs = (wave + KV_W * m) * 16;
+          bf16x8 KB[2], VB[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
-              P[qt][j] = e;
-              dS[qt][j] = e * dP[qt][j];
-            }
-        } else {
+          for (int s = 0; s < 2; ++s) {
+            KB[s] = ld_lds16(sm.K + krow_off(kabs + li, s * 4 + lg));
+            VB[s] = ld_lds16(sm.V + krow_off(kabs + li, s * 4 + lg));
+          }
+          f32x4 S[2], dP[2];
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt)
+          for (int qt = 0; qt < 2; ++qt) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = mfma16(Qa[qt][0], KB[0], z);
+            S[qt] = mfma16(Qa[qt][1], KB[1], z);
+            // the accumulator starts at -Delta, so it ends at dP - Delta
+            f32x4 y = ndl4[qt];
+            y = mfma16(dOa[qt][0], VB[0], y);
+            dP[qt] = mfma16(dOa[qt][1], VB[1], y);
+          }
+          f32x4 P[2], dS[2];
+          if (tile_all_visible(md, qlo, qhi, kabs, kabs + 16)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int qp = row_pos(r0 + qt * 16 + lg * 4 + j, p.inv_g);
-              const bool vis = visible_op<OP>(md, qp, kabs + li);
-              const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
-              const float pv = vis ? e : 0.f;
-              P[qt][j] = pv;
-              dS[qt][j] = pv * dP[qt][j];
-            }
+            for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
+                P[qt][j] = e;
+                dS[qt][j] = e * dP[qt][j];
+              }
+          } else {
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int qp = row_pos(r0 + qt * 16 + lg * 4 + j, p.inv_g);
+                const bool vis = visible_op<OP>(md, qp, kabs + li);
+                const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
+                const float pv = vis ? e : 0.f;
+                P[qt][j] = pv;
+                dS[qt][j] = pv * dP[qt][j];
+              }
+          }
+          Pb[m] = pack8(P[0], P[1]);
+          dSb[m] = pack8(dS[0], dS[1]);
         }
-        const bf16x8 Pb = pack8(P[0], P[1]);
-        const bf16x8 dSb = pack8(dS[0], dS[1]);
+      }
+      // 2. dV^T += dO^T P and dK^T += Q^T dS, one head-dim slice at a time
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          dVT[m][dt] = mfma16(dOTa[dt], Pb, dVT[m][dt]);
-          dKT[m][dt] = mfma16(QTa[dt], dSb, dKT[m][dt]);
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 qta = ld_lds16(b.QT + tr_off(dt * 16 + li, lg * 8));
+        const bf16x8 dota = ld_lds16(b.dOT + tr_off(dt * 16 + li, lg * 8));
+#pragma unroll
+        for (int m = 0; m < KV_TPW; ++m) {
+          if (!work[m]) continue;
+          dVT[m][dt] = mfma16(dota, Pb[m], dVT[m][dt]);
+          dKT[m][dt] = mfma16(qta, dSb[m], dKT[m][dt]);
         }
       }
     }
     // next chunk into the other buffer (last read before the previous
     // barrier), then prefetch the one after
-    if (c + 1 < c_end) {
-      stage(buf[(c + 1 - c_begin) & 1]);
-      if (c + 2 < c_end) fetch(c + 2);
+    if (c + 1 < nchunks) {
+      stage(sm.buf[(c + 1) & 1]);
+      if (c + 2 < nchunks) fetch(c + 2);
     }
     __syncthreads();
   }
 
 #pragma unroll
   for (int m = 0; m < KV_TPW; ++m) {
-    const int key = tile[m] * 16 + li;
-    if (!town[m] || key >= p.L) continue;
+    const int key = (wave + KV_W * m) * 16 + li;
+    if (key >= p.L) continue;
     bf16* dkd = p.dk + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
     bf16* dvd = p.dv + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
 #pragma unroll
@@ -507,10 +513,9 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.rows_per_split = per * DQ_QC;
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
   const long g1 = problems * p.splits;
-  // dkv kernel: enough workgroups per problem to give every wave its tiles
-  const int nkt = (p.L + 15) / 16;
-  p.nwg = max(1, (nkt + KV_W * KV_TPW - 1) / (KV_W * KV_TPW));
-  const long g2 = problems * p.nwg;
+  // dkv kernel: one workgroup per problem (20 tile slots cover 320 keys)
+  p.nwg = 1;
+  const long g2 = problems;
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 
   if (d.op == OP_SPACE) {
