@@ -166,27 +166,42 @@ void attn_bwd_dq_kernel(BwdParams p) {
     int klo, khi;
     key_range(md, qlo, qhi, klo, khi);
     const int st0 = klo >> 5, st1 = (khi + 31) >> 5;
+    // operands of one 32-key step: K and V rows (A of S^T, dP^T) for both
+    // 16-key halves, and K^T (A of dQ^T) for the four head-dim tiles; the
+    // next step's are loaded while this one computes
+    bf16x8 ka[2][2], va[2][2], kta[4];
+    auto load_step = [&](int kabs) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kr = kabs + h * 16 + li;
+        ka[h][0] = ld_lds16(sm.K + krow_off(kr, lg));
+        ka[h][1] = ld_lds16(sm.K + krow_off(kr, 4 + lg));
+        va[h][0] = ld_lds16(sm.V + krow_off(kr, lg));
+        va[h][1] = ld_lds16(sm.V + krow_off(kr, 4 + lg));
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) kta[dt] = ld_lds16(sm.KT + kt_off(dt * 16 + li, kabs + lg * 8));
+    };
+    if (st0 < st1) load_step(st0 * 32);
     for (int st = st0; st < st1; ++st) {
       const int kabs = st * 32;
       f32x4 sc[2][2], dp[2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kr = kabs + h * 16 + li;
-        const bf16x8 k0 = ld_lds16(sm.K + krow_off(kr, lg));
-        const bf16x8 k1 = ld_lds16(sm.K + krow_off(kr, 4 + lg));
-        const bf16x8 v0 = ld_lds16(sm.V + krow_off(kr, lg));
-        const bf16x8 v1 = ld_lds16(sm.V + krow_off(kr, 4 + lg));
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = mfma16(k0, qreg[qt][0], z);
-          sc[qt][h] = mfma16(k1, qreg[qt][1], z);
+          z = mfma16(ka[h][0], qreg[qt][0], z);
+          sc[qt][h] = mfma16(ka[h][1], qreg[qt][1], z);
           // the accumulator starts at -Delta, so it ends at dP - Delta
           f32x4 y = {-dlt[qt], -dlt[qt], -dlt[qt], -dlt[qt]};
-          y = mfma16(v0, dreg[qt][0], y);
-          dp[qt][h] = mfma16(v1, dreg[qt][1], y);
+          y = mfma16(va[h][0], dreg[qt][0], y);
+          dp[qt][h] = mfma16(va[h][1], dreg[qt][1], y);
         }
-      }
+      bf16x8 kt_cur[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) kt_cur[dt] = kta[dt];
+      if (st + 1 < st1) load_step(kabs + 32);
       bf16x8 dsb[2];
       if (tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
 #pragma unroll
@@ -217,9 +232,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 kt = ld_lds16(sm.KT + kt_off(dt * 16 + li, kabs + lg * 8));
-        acc[dt][0] = mfma16(kt, dsb[0], acc[dt][0]);
-        acc[dt][1] = mfma16(kt, dsb[1], acc[dt][1]);
+        acc[dt][0] = mfma16(kt_cur[dt], dsb[0], acc[dt][0]);
+        acc[dt][1] = mfma16(kt_cur[dt], dsb[1], acc[dt][1]);
       }
     }
 #pragma unroll
