@@ -12,15 +12,16 @@
 // unit is a block (space: positions = the N tokens of one frame) or a token
 // slot (time: positions = the T frames).  Its G = Hq/Hkv query heads are
 // folded into rows r = position * G + head-in-group, so that the K/V of the
-// group, staged once in LDS, serve all G heads.  A workgroup (4 waves) owns a
-// contiguous row range of one problem; each wave takes 64-row chunks and
-// sweeps the visible keys in 32-key steps.
+// group, staged once in LDS, serve all G heads.  A workgroup owns a
+// contiguous row range of one problem; each of its 8 waves takes 32-row
+// chunks and sweeps the visible keys in 32-key steps.
 //
 // Per step and wave: S^T (keys x queries) = K Q^T on MFMA with K from LDS and
 // Q^T from registers, so every lane holds one query column and the row
 // statistics need only a 4-lane reduction; online softmax in the log2 domain
-// with a lazy rescale (the running reference max is moved only when a new
-// score exceeds it by more than 2^8, which keeps exp2 arguments <= 8);
+// with a lazy rescale (a row's running reference max is moved only when one
+// of its new scores exceeds it by more than 2^8, which keeps exp2 arguments
+// <= 8; rows never rescale because of other rows' scores);
 // O^T += V^T P^T on MFMA with V^T from LDS.  Fully masked key steps are never
 // visited (causal and window ranges), and per-element masks are applied only
 // on steps that straddle a mask edge.
@@ -31,9 +32,10 @@ namespace bca {
 
 namespace {
 
-constexpr int KMAX = 320;      // keys resident in LDS per pass
-constexpr int QCH = 64;        // query rows per wave and chunk
-constexpr int NQT = QCH / 16;  // 16-column query tiles per chunk
+constexpr int KMAX = 320;   // keys resident in LDS per pass
+constexpr int FW = 8;       // waves per workgroup
+constexpr int QCH = 32;     // query rows per wave and chunk
+constexpr int NQT = QCH / 16;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 struct FwdParams {
@@ -42,9 +44,9 @@ struct FwdParams {
   const bf16* v;
   bf16* o;
   float* lse;
-  int op, T, N, Hq, Hkv, G, L, units, rows;
+  int T, N, Hq, Hkv, G, L, units, rows;
   int window, agent_begin, agent_count;
-  float scale_log2;
+  float scale_log2, inv_g;
   int splits, rows_per_split;
 };
 
@@ -63,17 +65,22 @@ __device__ __forceinline__ int vt_off(int d, int pos) {  // sVT: [64][KMAX]
   return d * KMAX + ((((pos >> 3) ^ (d & 7))) << 3) + (pos & 7);
 }
 
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
+// 8 waves of 32 query rows; two workgroups (80 KB of LDS each) share a CU,
+// so each SIMD interleaves four waves.
+template <int OP>
+__global__ __attribute__((amdgpu_flat_work_group_size(FW * 64, FW * 64), amdgpu_waves_per_eu(4, 4)))
+void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sK[KMAX * 64];
   __shared__ __attribute__((aligned(16))) bf16 sVT[64 * KMAX];
+  constexpr int NT = FW * 64;
 
   int ug, split;
   xcd_remap(blockIdx.x, p.units * p.Hkv, p.splits, ug, split);
   const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
-  const UnitGeom gq = unit_geom(p.op, u, p.T, p.N, p.Hq, 64);
-  const UnitGeom gk = unit_geom(p.op, u, p.T, p.N, p.Hkv, 64);
-  const UnitGeom gl = unit_geom(p.op, u, p.T, p.N, p.Hq, 1);
-  const MaskDesc md{p.op, p.L, p.window, p.agent_begin, p.agent_count};
+  const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, 64);
+  const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
+  const UnitGeom gl = unit_geom(OP, u, p.T, p.N, p.Hq, 1);
+  const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
   const bf16* kbase = p.k + gk.base + g * 64;
   const bf16* vbase = p.v + gk.base + g * 64;
   const bf16* qbase = p.q + gq.base + (int64_t)g * p.G * 64;
@@ -86,17 +93,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
   const int li = lane & 15, lg = lane >> 4;
   const int nkb = (p.L + KMAX - 1) / KMAX;
   const int nch = (row1 - row0 + QCH - 1) / QCH;
-  const int passes = (nch + 3) >> 2;
+  const int passes = (nch + FW - 1) / FW;
   const int G = p.G;
 
   for (int pass = 0; pass < passes; ++pass) {
-    const int ch = pass * 4 + wave;
+    const int ch = pass * FW + wave;
     const bool active = ch < nch;
     const int r0 = row0 + ch * QCH;
 
-    // Q^T operands, query positions and state for this chunk
+    // this lane's query column in each 16-column tile; padding columns read
+    // a real (clamped) row and are never stored
     bf16x8 qreg[NQT][2];
-    int qpos[NQT];
+    int qpos[NQT], hh[NQT];
     bool qvalid[NQT];
     f32x4 acc[NQT][4];
     float m[NQT], l[NQT];
@@ -106,12 +114,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       for (int qt = 0; qt < NQT; ++qt) {
         const int r = r0 + qt * 16 + li;
         qvalid[qt] = r < row1;
-        const int rr = qvalid[qt] ? r : row0;
-        qpos[qt] = rr / G;
-        const int hh = rr - qpos[qt] * G;
-        const bf16* src = qbase + qpos[qt] * gq.pos_stride + hh * 64 + lg * 8;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) qreg[qt][s] = qvalid[qt] ? ld_global16(src + s * 32) : zero8();
+        const int rr = min(r, row1 - 1);
+        qpos[qt] = row_pos(rr, p.inv_g);
+        hh[qt] = rr - qpos[qt] * G;
+        const bf16* src = qbase + qpos[qt] * gq.pos_stride + hh[qt] * 64 + lg * 8;
+        qreg[qt][0] = ld_global16(src);
+        qreg[qt][1] = ld_global16(src + 32);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[qt] = -INFINITY;
@@ -127,7 +135,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       if (nkb > 1 || pass == 0) {
         if (nkb > 1) __syncthreads();
         const int lp = (kn + 31) & ~31;
-        for (int idx = tid; idx < lp * 8; idx += 256) {
+        for (int idx = tid; idx < lp * 8; idx += NT) {
           const int r = idx >> 3, c = idx & 7;
           bf16x8 kv = zero8(), vv = zero8();
           if (r < kn) {
@@ -166,35 +174,39 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
           }
         }
         if (!tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
+          // a select, not a conditional store: hipcc dropped conditional
+          // element stores into this array of vectors
 #pragma unroll
           for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
-              for (int j = 0; j < 4; ++j)
-              {
-                // a select, not a conditional store: hipcc dropped conditional
-                // element stores into this array of vectors
-                const bool vis = visible(md, qpos[qt], kabs + h * 16 + lg * 4 + j);
+              for (int j = 0; j < 4; ++j) {
+                const bool vis = visible_op<OP>(md, qpos[qt], kabs + h * 16 + lg * 4 + j);
                 const float cur = sc[qt][h][j];
                 sc[qt][h][j] = vis ? cur : -INFINITY;
               }
         }
-        // online softmax with a lazy reference max (log2 domain)
+        // online softmax with a lazy reference max (log2 domain): a row's
+        // reference moves only when one of its scores exceeds it by more
+        // than 2^8, and only that row is rescaled (the others multiply by
+        // exactly 1), so every row depends on its own scores alone
         float mx[NQT];
-        bool grow = false;
+        bool grow[NQT];
+        bool any = false;
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
-          float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
-          float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
+          const float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
+          const float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
           mx[qt] = group4_max(fmaxf(a, b)) * p.scale_log2;
-          grow |= mx[qt] > m[qt] + kRescaleThreshold;
+          grow[qt] = mx[qt] > m[qt] + kRescaleThreshold;
+          any |= grow[qt];
         }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
+        if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
           for (int qt = 0; qt < NQT; ++qt) {
-            const float mn = fmaxf(m[qt], mx[qt]);
-            const float alpha = (mn == -INFINITY) ? 1.f : fast_exp2(m[qt] - mn);
+            const float mn = grow[qt] ? mx[qt] : m[qt];
+            const float alpha = grow[qt] ? fast_exp2(m[qt] - mn) : 1.f;
             l[qt] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc[qt][dt] *= alpha;
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
             e0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -mref));
             e1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -mref));
           }
-          l[qt] += (e0[0] + e0[1]) + (e0[2] + e0[3]) + (e1[0] + e1[1]) + (e1[2] + e1[3]);
+          l[qt] += ((e0[0] + e0[1]) + (e0[2] + e0[3])) + ((e1[0] + e1[1]) + (e1[2] + e1[3]));
           pb[qt] = pack8(e0, e1);
         }
         // O^T += V^T P^T
@@ -229,16 +241,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(FwdParams p) {
       for (int qt = 0; qt < NQT; ++qt) {
         const float lt = group4_sum(l[qt]);
         if (!qvalid[qt]) continue;
-        const int r = r0 + qt * 16 + li;
-        const int hh = r - qpos[qt] * G;
         const float inv = 1.f / lt;
-        bf16* dst = obase + qpos[qt] * gq.pos_stride + hh * 64 + lg * 4;
+        bf16* dst = obase + qpos[qt] * gq.pos_stride + hh[qt] * 64 + lg * 4;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const bf16x4 o4 = pack4(acc[qt][dt] * inv);
           *reinterpret_cast<u32x2*>(dst + dt * 16) = __builtin_bit_cast(u32x2, o4);
         }
-        if (lg == 0) lbase[qpos[qt] * gl.pos_stride + hh] = (m[qt] + __log2f(lt)) * kLn2;
+        if (lg == 0) lbase[qpos[qt] * gl.pos_stride + hh[qt]] = (m[qt] + __log2f(lt)) * kLn2;
       }
     }
   }
@@ -254,7 +264,6 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.v = static_cast<const bf16*>(v);
   p.o = static_cast<bf16*>(o);
   p.lse = lse;
-  p.op = d.op;
   p.T = d.T;
   p.N = d.N;
   p.Hq = d.Hq;
@@ -267,19 +276,24 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.agent_begin = d.agent_begin;
   p.agent_count = d.agent_count;
   p.scale_log2 = d.scale * kLog2e;
+  p.inv_g = 1.0f / (float)p.G;
+  if (p.G > 256 || (long)p.rows >= (1L << 21)) return hipErrorInvalidValue;
   // Split each problem's rows over several workgroups so that the grid
-  // covers the 256 CUs about three times over (2 workgroups per CU fit).
-  const int problems = p.units * p.Hkv;
+  // covers the 256 CUs (two workgroups each) about three times over.
+  const long problems = (long)p.units * p.Hkv;
   const int chunks = (p.rows + QCH - 1) / QCH;
   int splits = (int)((3 * 512 + problems - 1) / problems);
-  splits = max(1, min(splits, (chunks + 3) / 4));
+  splits = max(1, min(splits, (chunks + FW - 1) / FW));
   int per = (chunks + splits - 1) / splits;
-  per = ((per + 3) / 4) * 4;  // whole passes of 4 chunks
+  per = ((per + FW - 1) / FW) * FW;  // whole passes of FW chunks
   p.rows_per_split = per * QCH;
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
-  const long grid = (long)problems * p.splits;
+  const long grid = problems * p.splits;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  if (d.op == OP_SPACE)
+    hipLaunchKernelGGL(attn_fwd_kernel<OP_SPACE>, dim3((unsigned)grid), dim3(FW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<OP_TIME>, dim3((unsigned)grid), dim3(FW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
