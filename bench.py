@@ -41,6 +41,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
 
 
+# kernel launches of each attention call (template argument 0 = space, 1 = time)
+KERNELS = {
+    "space_fwd": "attn_fwd_kernel<0>",
+    "time_fwd": "attn_fwd_kernel<1>",
+    "space_bwd": "attn_bwd_dq_kernel<0> + attn_bwd_dkv_kernel<0>",
+    "time_bwd": "attn_bwd_dq_kernel<1> + attn_bwd_dkv_kernel<1>",
+}
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
@@ -69,16 +78,16 @@ def read_traffic(kernel_key: str):
     return float(v) if v else None
 
 
-def cpu_baseline(target_s: float = 12.0):
-    """Time the fp64 oracle on a bounded sample of the same step (whole
-    blocks of the space layer and whole slots of the time layer)."""
-    import numpy as np
+def cpu_baseline(target_s: float = 15.0):
+    """Time the fp64 oracle on a bounded sample of the same step: n whole
+    blocks of the space layer and n whole slots of the time layer, fwd + bwd,
+    with n chosen from a short probe run so the sample takes ~target_s."""
     from block_causal_transformer_amd import configs as C, gen
     from oracle import oracle as O
 
-    def run(nb, ns):
-        ws = C.get("3").with_(B=1, T=nb)
-        wt = C.get("4").with_(N=ns)
+    def run(n):
+        ws = C.get("3").with_(B=1, T=n)
+        wt = C.get("4").with_(N=n)
         xs, xt = gen.make_inputs(ws), gen.make_inputs(wt)
         t0 = time.perf_counter()
         O.fwd(ws, xs["q"], xs["k"], xs["v"])
@@ -89,16 +98,16 @@ def cpu_baseline(target_s: float = 12.0):
         fl = sum(C.flops(w, d) for w in (ws, wt) for d in ("fwd", "bwd"))
         return dt, fl
 
-    dt, fl = run(1, 1)
-    scale = max(1, min(64, int(target_s / max(dt, 1e-3))))
-    dt, fl = run(scale, scale)
+    dt, _ = run(4)
+    n = max(4, min(256, int(4 * target_s / max(dt, 1e-3))))
+    dt, fl = run(n)
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": O.max_threads(),
         "kind": "oracle",
-        "sample": "%d space blocks (290 tokens) + %d time slots (256 frames), fwd+bwd, fp64, %.1f s"
-                  % (scale, scale, dt),
+        "sample": "%d space blocks (290 tokens, 30 q / 3 kv heads) + %d time slots (256 frames, "
+                  "window 192), forward + backward, fp64, %.1f s" % (n, n, dt),
     }
 
 
@@ -222,7 +231,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(d["min_bytes"] / d["ms"] / 1e6, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = dom
+    roof["kernel"] = dom + " (" + KERNELS[dom] + ")"
     roof["traffic"] = read_traffic(dom)
 
     out = {

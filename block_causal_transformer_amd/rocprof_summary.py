@@ -1,0 +1,170 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
+
+    python -m block_causal_transformer_amd.rocprof_summary stats \\
+        KERNEL_STATS_CSV OUT_MD --cmd "the profiled command"
+    python -m block_causal_transformer_amd.rocprof_summary traffic \\
+        FETCH_COUNTER_CSV WRITE_COUNTER_CSV OUT_TXT --cmd "..."
+
+``stats`` lists every kernel of a ``--kernel-trace --stats`` run (calls,
+average and total duration).  ``traffic`` reads two ``--pmc FETCH_SIZE`` /
+``--pmc WRITE_SIZE`` runs of ``bench.py --copy-probe-mib M`` and writes HBM
+bytes per launch of each attention op, each counter scaled by the factor
+that makes it read the known byte count of the plain device copy of M MiB
+that the same run performs; ``bench.py`` reads that file for the roofline's
+``traffic`` field (and ignores it once the kernel sources change).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
+
+# attention op of each kernel (template argument 0 = space, 1 = time)
+OPS = [
+    (r"attn_fwd_kernel<0>", "space_fwd"),
+    (r"attn_fwd_kernel<1>", "time_fwd"),
+    (r"attn_bwd_dq_kernel<0>", "space_bwd"),
+    (r"attn_bwd_dkv_kernel<0>", "space_bwd"),
+    (r"attn_bwd_dq_kernel<1>", "time_bwd"),
+    (r"attn_bwd_dkv_kernel<1>", "time_bwd"),
+]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(kernel: str) -> str:
+    k = kernel.replace("void ", "").replace("bca::(anonymous namespace)::", "")
+    k = k.split("(bca::")[0]
+    if len(k) > 90:
+        k = k[:87] + "..."
+    return k
+
+
+def op_of(kernel: str):
+    k = short_name(kernel)
+    for pat, op in OPS:
+        if k.startswith(pat):
+            return op
+    return None
+
+
+def cmd_stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["# rocprofv3 kernel statistics", "",
+           "Command (run from the repository root on one MI355X):", "",
+           "    " + args.cmd, "",
+           "| kernel | op | calls | average (us) | total (us) | share |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| `%s` | %s | %s | %.1f | %.1f | %.1f%% |" % (
+            short_name(r["Name"]), op_of(r["Name"]) or "-", r["Calls"],
+            float(r["AverageNs"]) / 1e3, float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
+    per_op = collections.defaultdict(float)
+    for r in rows:
+        op = op_of(r["Name"])
+        if op:
+            per_op[op] += float(r["AverageNs"]) / 1e3
+    out += ["", "Average duration per attention op (sum over its kernels):", "",
+            "| op | average (us) |", "|---|---|"]
+    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd"):
+        if op in per_op:
+            out.append("| %s | %.1f |" % (op, per_op[op]))
+    out.append("")
+    with open(args.out, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+
+
+def _counter(path, name):
+    """(kernel name, value) per dispatch for counter ``name``."""
+    res = []
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == name:
+            res.append((r["Kernel_Name"], float(r["Counter_Value"]), int(r["Dispatch_Id"])))
+    return res
+
+
+def cmd_traffic(args):
+    probe = args.copy_mib * (1 << 20)
+    vals = {}
+    for path, cname in ((args.fetch_csv, "FETCH_SIZE"), (args.write_csv, "WRITE_SIZE")):
+        rows = _counter(path, cname)
+        copies = [v for (k, v, _) in rows if "copy" in k.lower()]
+        if not copies:
+            sys.exit("no copy kernel found in %s" % path)
+        # the probe is the largest plain copy of the run
+        copy_kib = max(copies)
+        factor = probe / (copy_kib * 1024.0)
+        per_op = collections.defaultdict(list)
+        per_disp = collections.defaultdict(float)
+        for k, v, d in rows:
+            op = op_of(k)
+            if op:
+                per_disp[(op, d)] += v
+        # one launch of an op = its kernels' dispatches; average over launches
+        for (op, d), v in per_disp.items():
+            per_op[(op, short_name([k for k, _, dd in rows if dd == d][0]))].append(v)
+        vals[cname] = (copy_kib, factor, per_op)
+    out = ["# HBM traffic per launch, from rocprofv3 counters", "#",
+           "# commands (from the repository root, one MI355X):",
+           "#   " + args.cmd.replace("COUNTER", "FETCH_SIZE"),
+           "#   " + args.cmd.replace("COUNTER", "WRITE_SIZE"),
+           "# Each counter (KiB per dispatch) is scaled by the factor that makes it",
+           "# read %d bytes for the plain %d MiB device copy in the same run." % (probe, args.copy_mib),
+           "source_sha=%s" % source_digest(),
+           "copy_probe_bytes=%d" % probe]
+    for cname, (ck, fac, _) in vals.items():
+        out.append("%s.copy_kib=%.1f" % (cname.lower(), ck))
+        out.append("%s.factor=%.4f" % (cname.lower(), fac))
+    ops = collections.defaultdict(float)
+    for cname, (_, fac, per_op) in vals.items():
+        for (op, kname), vs in sorted(per_op.items()):
+            avg = sum(vs) / len(vs)
+            out.append("%s.%s.kib_per_dispatch=%.1f  # %s" % (op, cname.lower(), avg, kname))
+            ops[op] += avg * 1024.0 * fac
+    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd"):
+        if op in ops:
+            out.append("%s.bytes=%.0f" % (op, ops[op]))
+    out.append("")
+    with open(args.out, "w") as f:
+        f.write("\n".join(out))
+    print("\n".join(out))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    a.add_argument("out")
+    a.add_argument("--cmd", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("out")
+    b.add_argument("--cmd", required=True)
+    b.add_argument("--copy-mib", type=int, default=2048)
+    args = ap.parse_args(argv)
+    if args.what == "stats":
+        cmd_stats(args)
+    else:
+        cmd_traffic(args)
+
+
+if __name__ == "__main__":
+    main()
