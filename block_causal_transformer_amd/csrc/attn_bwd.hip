@@ -28,7 +28,9 @@
 //             registers; the problem's query rows stream through LDS in
 //             32-row chunks (double-buffered, prefetched into registers one
 //             chunk ahead): S = Q K^T and dP = dO V^T, then dV^T += dO^T P
-//             and dK^T += Q^T dS on MFMA.
+//             and dK^T += Q^T dS on MFMA, with the Q^T and dO^T operands
+//             read straight from the row-major chunk by transposing LDS
+//             reads.
 //
 // Key steps (dq) and query chunks (dkv) that the causal / window ranges make
 // invisible are never visited.  The split costs two more matmul passes than a
@@ -256,21 +258,19 @@ constexpr int KV_QC = 32;  // query rows per chunk
 __device__ __forceinline__ int row_off(int row, int chunk) {  // [32][64]
   return row * 64 + ((chunk ^ (row & 7)) << 3);
 }
-// Transposed chunk rows: query q of the chunk sits at position
-// 8*((q>>2)&3) + 4*(q>>4) + (q&3), so the 8 queries a lane feeds to one
-// MFMA (q = 16h + 4g + j) are contiguous.
-__device__ __forceinline__ int tq_perm(int q) {
-  return (((q >> 2) & 3) << 3) | ((q >> 4) << 2) | (q & 3);
-}
-__device__ __forceinline__ int tr_off(int d, int pos) {  // [64][32]
-  return d * 32 + ((((pos >> 3) ^ (d & 3))) << 3) + (pos & 7);
+// Offset of the 8-byte piece this lane addresses in a transposing read of
+// the row-major chunk tile: rows 16*h + 4*g + (li >> 2), columns
+// 16*dt + 4*(li & 3) .. +3.  Lane (li, g) then receives column 16*dt + li of
+// rows 16*h + 4*g + 0..3, i.e. four of the 8 queries it feeds to one MFMA.
+__device__ __forceinline__ int tr_piece_off(int h, int dt, int li, int lg) {
+  const int row = 16 * h + 4 * lg + (li >> 2);
+  const int col = 16 * dt + 4 * (li & 3);
+  return row * 64 + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
 }
 
 struct KvBuf {
   bf16 Q[KV_QC * 64];
   bf16 dO[KV_QC * 64];
-  bf16 QT[64 * KV_QC];
-  bf16 dOT[64 * KV_QC];
   float lse[KV_QC];
   float delta[KV_QC];
 };
@@ -350,12 +350,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     }
   };
   auto stage = [&](KvBuf& b) {
-    const int tp = tq_perm(srow);
-    bf16* rowm = carries_q ? b.Q : b.dO;
-    bf16* trm = carries_q ? b.QT : b.dOT;
-    st_lds16(rowm + row_off(srow, sch), pre);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) trm[tr_off(sch * 8 + e, tp)] = pre[e];
+    st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
     if (sch == 0) (carries_q ? b.lse : b.delta)[srow] = pre_s;
   };
 
@@ -447,8 +442,9 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       // 2. dV^T += dO^T P and dK^T += Q^T dS, one head-dim slice at a time
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 qta = ld_lds16(b.QT + tr_off(dt * 16 + li, lg * 8));
-        const bf16x8 dota = ld_lds16(b.dOT + tr_off(dt * 16 + li, lg * 8));
+        const int o0 = tr_piece_off(0, dt, li, lg), o1 = tr_piece_off(1, dt, li, lg);
+        const bf16x8 qta = join8(ld_lds_tr4(b.Q + o0), ld_lds_tr4(b.Q + o1));
+        const bf16x8 dota = join8(ld_lds_tr4(b.dO + o0), ld_lds_tr4(b.dO + o1));
 #pragma unroll
         for (int m = 0; m < KV_TPW; ++m) {
           if (!work[m]) continue;

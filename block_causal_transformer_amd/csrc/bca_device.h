@@ -83,6 +83,24 @@ __device__ __forceinline__ void st_lds16(bf16* p, const bf16x8& v) {
   *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
 }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of
+// 16 lanes, lane i receives as its element e the element (i & 3) of the
+// 8-byte piece addressed by lane 4*e + (i >> 2) of the same group.  So if
+// lane s addresses row R(s >> 2), columns c0 + 4*(s & 3) .. +3 of a
+// row-major bf16 tile, lane i receives column c0 + i of rows R(0..3): four
+// rows of one column, as an MFMA operand wants them.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 ld_lds_tr4(const bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 join8(const bf16x4& a, const bf16x4& b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // Element offsets of position 0 of a unit (a block for space attention, a
 // token slot for time attention) for a tensor with H heads of width D, and
 // the stride between positions.  Tensors are (B, T, N, H, D) row-major.
