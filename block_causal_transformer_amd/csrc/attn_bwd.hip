@@ -105,7 +105,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const bf16* kbase = p.k + gk.base + g * 64;
   const bf16* vbase = p.v + gk.base + g * 64;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
   const int lp32 = (p.L + 31) & ~31;
 
@@ -126,10 +127,34 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int row1 = min(p.rows, row0 + p.rows_per_split);
   const int nch = (row1 - row0 + DQ_QC - 1) / DQ_QC;
 
+  // Per chunk, this lane's query column in each of the two 16-column tiles
+  // (padding columns read a real, clamped row and are never stored).  The
+  // next chunk's Q, dO, O and LSE are loaded while the current one computes.
+  struct ChunkIn {
+    bf16x8 q[2][2], d[2][2], o[2][2];
+    float lse[2];
+  };
+  auto load_chunk = [&](int ch, ChunkIn& in) {
+    const int r0c = row0 + ch * DQ_QC;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int rr = min(r0c + qt * 16 + li, row1 - 1);
+      const int pos = row_pos(rr, p.inv_g);
+      const int hq = rr - pos * G;
+      const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hq * 64 + lg * 8;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        in.q[qt][s] = ld_global16(p.q + off + s * 32);
+        in.d[qt][s] = ld_global16(p.dout + off + s * 32);
+        in.o[qt][s] = ld_global16(p.o + off + s * 32);
+      }
+      in.lse[qt] = p.lse[gl.base + (int64_t)pos * gl.pos_stride + g * G + hq];
+    }
+  };
+  ChunkIn nxt;
+  if (wave < nch) load_chunk(wave, nxt);
   for (int ch = wave; ch < nch; ch += DQ_W) {
     const int r0 = row0 + ch * DQ_QC;
-    // this lane's query column in each of the two 16-column tiles; padding
-    // columns read a real row (clamped) and are never stored
     bf16x8 qreg[2][2], dreg[2][2];
     int qpos[2], hh[2];
     bool qv[2];
@@ -141,22 +166,20 @@ void attn_bwd_dq_kernel(BwdParams p) {
       const int rr = min(r, row1 - 1);
       qpos[qt] = row_pos(rr, p.inv_g);
       hh[qt] = rr - qpos[qt] * G;
-      const int64_t off = gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 8;
       float part = 0.f;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        qreg[qt][s] = ld_global16(p.q + off + s * 32);
-        dreg[qt][s] = ld_global16(p.dout + off + s * 32);
-        const bf16x8 ov = ld_global16(p.o + off + s * 32);
+        qreg[qt][s] = nxt.q[qt][s];
+        dreg[qt][s] = nxt.d[qt][s];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)dreg[qt][s][e], (float)ov[e], part);
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)nxt.d[qt][s][e], (float)nxt.o[qt][s][e], part);
       }
       dlt[qt] = group4_sum(part);
       const int64_t lo = gl.base + (int64_t)qpos[qt] * gl.pos_stride + g * G + hh[qt];
-      const float l = p.lse[lo];
-      lse2[qt] = qv[qt] ? l * kLog2e : INFINITY;
+      lse2[qt] = qv[qt] ? nxt.lse[qt] * kLog2e : INFINITY;
       if (qv[qt] && lg == 0) p.delta[lo] = dlt[qt];
     }
+    if (ch + DQ_W < nch) load_chunk(ch + DQ_W, nxt);
     f32x4 acc[4][2];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -168,42 +191,27 @@ void attn_bwd_dq_kernel(BwdParams p) {
     int klo, khi;
     key_range(md, qlo, qhi, klo, khi);
     const int st0 = klo >> 5, st1 = (khi + 31) >> 5;
-    // operands of one 32-key step: K and V rows (A of S^T, dP^T) for both
-    // 16-key halves, and K^T (A of dQ^T) for the four head-dim tiles; the
-    // next step's are loaded while this one computes
-    bf16x8 ka[2][2], va[2][2], kta[4];
-    auto load_step = [&](int kabs) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kr = kabs + h * 16 + li;
-        ka[h][0] = ld_lds16(sm.K + krow_off(kr, lg));
-        ka[h][1] = ld_lds16(sm.K + krow_off(kr, 4 + lg));
-        va[h][0] = ld_lds16(sm.V + krow_off(kr, lg));
-        va[h][1] = ld_lds16(sm.V + krow_off(kr, 4 + lg));
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) kta[dt] = ld_lds16(sm.KT + kt_off(dt * 16 + li, kabs + lg * 8));
-    };
-    if (st0 < st1) load_step(st0 * 32);
     for (int st = st0; st < st1; ++st) {
       const int kabs = st * 32;
       f32x4 sc[2][2], dp[2][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        const int kr = kabs + h * 16 + li;
+        const bf16x8 k0 = ld_lds16(sm.K + krow_off(kr, lg));
+        const bf16x8 k1 = ld_lds16(sm.K + krow_off(kr, 4 + lg));
+        const bf16x8 v0 = ld_lds16(sm.V + krow_off(kr, lg));
+        const bf16x8 v1 = ld_lds16(sm.V + krow_off(kr, 4 + lg));
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = mfma16(ka[h][0], qreg[qt][0], z);
-          sc[qt][h] = mfma16(ka[h][1], qreg[qt][1], z);
+          z = mfma16(k0, qreg[qt][0], z);
+          sc[qt][h] = mfma16(k1, qreg[qt][1], z);
           // the accumulator starts at -Delta, so it ends at dP - Delta
           f32x4 y = {-dlt[qt], -dlt[qt], -dlt[qt], -dlt[qt]};
-          y = mfma16(va[h][0], dreg[qt][0], y);
-          dp[qt][h] = mfma16(va[h][1], dreg[qt][1], y);
+          y = mfma16(v0, dreg[qt][0], y);
+          dp[qt][h] = mfma16(v1, dreg[qt][1], y);
         }
-      bf16x8 kt_cur[4];
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) kt_cur[dt] = kta[dt];
-      if (st + 1 < st1) load_step(kabs + 32);
+      }
       bf16x8 dsb[2];
       if (tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
 #pragma unroll
@@ -234,8 +242,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        acc[dt][0] = mfma16(kt_cur[dt], dsb[0], acc[dt][0]);
-        acc[dt][1] = mfma16(kt_cur[dt], dsb[1], acc[dt][1]);
+        const bf16x8 kt = ld_lds16(sm.KT + kt_off(dt * 16 + li, kabs + lg * 8));
+        acc[dt][0] = mfma16(kt, dsb[0], acc[dt][0]);
+        acc[dt][1] = mfma16(kt, dsb[1], acc[dt][1]);
       }
     }
 #pragma unroll
@@ -302,7 +311,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const bf16* kbase = p.k + gk.base + g * 64;
   const bf16* vbase = p.v + gk.base + g * 64;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
   const int nkt = (p.L + 15) >> 4;
   const int lp16 = nkt * 16;
@@ -516,7 +526,7 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   // dq kernel: one workgroup per CU (LDS), rows split so the grid covers the
   // CUs a few times over
   const int chunks = (p.rows + DQ_QC - 1) / DQ_QC;
-  int splits = (int)((3 * 256 + problems - 1) / problems);
+  int splits = (int)((6 * 256 + problems - 1) / problems);
   splits = max(1, min(splits, (chunks + DQ_W - 1) / DQ_W));
   int per = (chunks + splits - 1) / splits;
   per = ((per + DQ_W - 1) / DQ_W) * DQ_W;

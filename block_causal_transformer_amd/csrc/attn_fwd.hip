@@ -89,7 +89,8 @@ void attn_fwd_kernel(FwdParams p) {
 
   const int row0 = split * p.rows_per_split;
   const int row1 = min(p.rows, row0 + p.rows_per_split);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
   const int nkb = (p.L + KMAX - 1) / KMAX;
   const int nch = (row1 - row0 + QCH - 1) / QCH;
