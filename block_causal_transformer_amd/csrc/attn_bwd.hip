@@ -339,29 +339,43 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   // a piece is (row, 16-byte column chunk) of the chunk
   const bool carries_q = tid < 256;
   const int srow = (tid & 255) >> 3, sch = tid & 7;
+  // The loads are only issued here; the LSE transform waits for stage() so
+  // that no wave stalls on the global load a chunk early.
   bf16x8 pre = zero8();
   float pre_s = 0.f;
+  bool pre_valid = false;
   auto fetch = [&](int c) {
     // padding rows read a real (clamped) row; their LSE of +inf zeroes P
     const int r = c * KV_QC + srow;
-    const bool valid = r < p.rows;
+    pre_valid = r < p.rows;
     const int rr = min(r, p.rows - 1);
     const int pos = row_pos(rr, p.inv_g);
     const int hh = rr - pos * G;
     const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + sch * 8;
     const int64_t lo = gl.base + (int64_t)pos * gl.pos_stride + g * G + hh;
-    if (carries_q) {
-      pre = ld_global16(p.q + off);
-      const float l = p.lse[lo];
-      pre_s = valid ? l * kLog2e : INFINITY;
-    } else {
-      pre = ld_global16(p.dout + off);
-      pre_s = p.delta[lo];
-    }
+    pre = ld_global16((carries_q ? p.q : p.dout) + off);
+    pre_s = carries_q ? p.lse[lo] : p.delta[lo];
   };
   auto stage = [&](KvBuf& b) {
     st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
-    if (sch == 0) (carries_q ? b.lse : b.delta)[srow] = pre_s;
+    if (sch == 0) {
+      if (carries_q)
+        b.lse[srow] = pre_valid ? pre_s * kLog2e : INFINITY;
+      else
+        b.delta[srow] = pre_s;
+    }
+  };
+
+  // K and V operands of the next slot are read while this one computes, and
+  // those of slot 0 at the end of the previous chunk (a slot past the last
+  // tile reads the last tile and is skipped)
+  auto load_kv = [&](int m, bf16x8* kb, bf16x8* vb) {
+    const int key = min(wave + KV_W * m, nkt - 1) * 16 + li;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      kb[s] = ld_lds16(sm.K + krow_off(key, s * 4 + lg));
+      vb[s] = ld_lds16(sm.V + krow_off(key, s * 4 + lg));
+    }
   };
 
   const int nchunks = (p.rows + KV_QC - 1) / KV_QC;
@@ -369,6 +383,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   stage(sm.buf[0]);
   if (1 < nchunks) fetch(1);
   __syncthreads();
+  bf16x8 KB0[2], VB0[2];
+  load_kv(0, KB0, VB0);
 
   for (int c = 0; c < nchunks; ++c) {
     KvBuf& b = sm.buf[c & 1];
@@ -401,16 +417,13 @@ void attn_bwd_dkv_kernel(BwdParams p) {
           lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
           ndl4[qt] = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
         }
+        bf16x8 KB[2] = {KB0[0], KB0[1]}, VB[2] = {VB0[0], VB0[1]};
 #pragma unroll
         for (int m = 0; m < KV_TPW; ++m) {
-          if (!work[m]) continue;
+          bf16x8 KBn[2], VBn[2];
+          if (m + 1 < KV_TPW) load_kv(m + 1, KBn, VBn);
+          if (work[m]) {
           const int kabs = (wave + KV_W * m) * 16;
-          bf16x8 KB[2], VB[2];
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            KB[s] = ld_lds16(sm.K + krow_off(kabs + li, s * 4 + lg));
-            VB[s] = ld_lds16(sm.V + krow_off(kabs + li, s * 4 + lg));
-          }
           f32x4 S[2], dP[2];
 #pragma unroll
           for (int qt = 0; qt < 2; ++qt) {
@@ -447,24 +460,37 @@ void attn_bwd_dkv_kernel(BwdParams p) {
           }
           Pb[m] = pack8(P[0], P[1]);
           dSb[m] = pack8(dS[0], dS[1]);
+          }
+          if (m + 1 < KV_TPW) {
+            KB[0] = KBn[0];
+            KB[1] = KBn[1];
+            VB[0] = VBn[0];
+            VB[1] = VBn[1];
+          }
         }
       }
-      // 2. dV^T += dO^T P and dK^T += Q^T dS, one head-dim slice at a time
+      // 2. dV^T += dO^T P and dK^T += Q^T dS; all transposed operands are
+      // read first so that one LDS round trip covers the whole phase
+      bf16x8 qta[4], dota[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const int o0 = tr_piece_off(0, dt, li, lg), o1 = tr_piece_off(1, dt, li, lg);
-        const bf16x8 qta = join8(ld_lds_tr4(b.Q + o0), ld_lds_tr4(b.Q + o1));
-        const bf16x8 dota = join8(ld_lds_tr4(b.dO + o0), ld_lds_tr4(b.dO + o1));
+        qta[dt] = join8(ld_lds_tr4(b.Q + o0), ld_lds_tr4(b.Q + o1));
+        dota[dt] = join8(ld_lds_tr4(b.dO + o0), ld_lds_tr4(b.dO + o1));
+      }
 #pragma unroll
-        for (int m = 0; m < KV_TPW; ++m) {
-          if (!work[m]) continue;
-          dVT[m][dt] = mfma16(dota, Pb[m], dVT[m][dt]);
-          dKT[m][dt] = mfma16(qta, dSb[m], dKT[m][dt]);
+      for (int m = 0; m < KV_TPW; ++m) {
+        if (!work[m]) continue;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          dVT[m][dt] = mfma16(dota[dt], Pb[m], dVT[m][dt]);
+          dKT[m][dt] = mfma16(qta[dt], dSb[m], dKT[m][dt]);
         }
       }
     }
     // next chunk into the other buffer (last read before the previous
     // barrier), then prefetch the one after
+    load_kv(0, KB0, VB0);
     if (c + 1 < nchunks) {
       stage(sm.buf[(c + 1) & 1]);
       if (c + 2 < nchunks) fetch(c + 2);
