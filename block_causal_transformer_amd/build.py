@@ -4,7 +4,9 @@
 
 Each source is compiled to an object under ``_build/`` (in parallel), then
 linked into ``block_causal_transformer_amd/libbca.so``.  Device code is built
-with packed-fp32 instructions disabled.
+with packed-fp32 instructions disabled.  The device assembly of every HIP
+source is also generated and checked for MFMA results read too early
+(``hazard_check``); a hit fails the build.
 """
 from __future__ import annotations
 
@@ -17,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
+ASM = os.path.join(ROOT, "_build", "asm")
 LIB = os.path.join(PKG, "libbca.so")
 SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_generic.hip", "bca_abi.cpp"]
 ARCH = os.environ.get("BCA_OFFLOAD_ARCH", "gfx950")
@@ -31,9 +34,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", out]
+    if src.startswith("asm:"):
+        src = src[4:]
+        out = os.path.join(ASM, os.path.splitext(src)[0] + ".s")
+        cmd = [HIPCC] + COMMON + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    noise = ("is not a recognized feature for this target", "argument unused during compilation: '--hip-link'")
+    err = "\n".join(l for l in r.stderr.splitlines() if not any(n in l for n in noise))
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
     if err.strip():
@@ -42,9 +49,20 @@ def _compile(src: str) -> str:
 
 
 def build(verbose: bool = True) -> str:
+    from . import hazard_check
+
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    os.makedirs(ASM, exist_ok=True)
+    jobs = SOURCES + ["asm:" + s for s in SOURCES if s.endswith(".hip")]
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
+        outs = list(ex.map(_compile, jobs))
+    objs = [o for o in outs if o.endswith(".o")]
+    for path in (o for o in outs if o.endswith(".s")):
+        bad = hazard_check.check_file(path)
+        if bad:
+            lines = ["%s: %s: %s -> %s (after %d wait states)" % (os.path.basename(path), k, b[0][0], b[0][1], b[0][2])
+                     for k, b in bad.items()]
+            raise RuntimeError("MFMA result read too early in the device code:\n" + "\n".join(lines))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

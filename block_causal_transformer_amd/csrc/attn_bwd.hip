@@ -35,7 +35,8 @@
 // Key steps (dq) and query chunks (dkv) that the causal / window ranges make
 // invisible are never visited.  The split costs two more matmul passes than a
 // fused kernel (S and dP are formed in both) in exchange for half the
-// register footprint per wave, no LDS exchange of dS, and two waves per SIMD.
+// register footprint per wave, no LDS exchange of dS, and two (dkv) or three
+// (dq) waves per SIMD.
 #include "bca_device.h"
 #include "bca_kernels.h"
 
@@ -60,12 +61,11 @@ struct BwdParams {
   int window, agent_begin, agent_count;
   float scale, scale_log2, inv_g;
   int splits, rows_per_split;  // dq kernel
-  int nwg;                     // dkv kernel: workgroups per problem (1)
 };
 
 // ------------------------------------------------------------- dq kernel
 
-constexpr int DQ_W = 8;    // waves per workgroup
+constexpr int DQ_W = 12;   // waves per workgroup
 constexpr int DQ_QC = 32;  // query rows per wave and chunk
 
 __device__ __forceinline__ int krow_off(int key, int chunk) {  // [KMAX][64], 16B chunks xor-swizzled
@@ -88,7 +88,7 @@ struct DqSmem {
 };
 
 template <int OP>
-__global__ __attribute__((amdgpu_flat_work_group_size(DQ_W * 64, DQ_W * 64), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(DQ_W * 64, DQ_W * 64), amdgpu_waves_per_eu(3, 3)))
 void attn_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   constexpr int NT = DQ_W * 64;
@@ -151,10 +151,10 @@ void attn_bwd_dq_kernel(BwdParams p) {
       in.lse[qt] = p.lse[gl.base + (int64_t)pos * gl.pos_stride + g * G + hq];
     }
   };
-  ChunkIn nxt;
-  if (wave < nch) load_chunk(wave, nxt);
   for (int ch = wave; ch < nch; ch += DQ_W) {
     const int r0 = row0 + ch * DQ_QC;
+    ChunkIn nxt;
+    load_chunk(ch, nxt);
     bf16x8 qreg[2][2], dreg[2][2];
     int qpos[2], hh[2];
     bool qv[2];
@@ -175,11 +175,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
         for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)nxt.d[qt][s][e], (float)nxt.o[qt][s][e], part);
       }
       dlt[qt] = group4_sum(part);
-      const int64_t lo = gl.base + (int64_t)qpos[qt] * gl.pos_stride + g * G + hh[qt];
       lse2[qt] = qv[qt] ? nxt.lse[qt] * kLog2e : INFINITY;
-      if (qv[qt] && lg == 0) p.delta[lo] = dlt[qt];
     }
-    if (ch + DQ_W < nch) load_chunk(ch + DQ_W, nxt);
     f32x4 acc[4][2];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -247,9 +244,12 @@ void attn_bwd_dq_kernel(BwdParams p) {
         acc[dt][1] = mfma16(kt, dsb[1], acc[dt][1]);
       }
     }
+    // Delta is stored only now so that no wait on the store delays the
+    // first products of the chunk
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       if (!qv[qt]) continue;
+      if (lg == 0) p.delta[gl.base + (int64_t)qpos[qt] * gl.pos_stride + g * G + hh[qt]] = dlt[qt];
       bf16* dst = p.dq + gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 4;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -284,20 +284,21 @@ struct KvBuf {
   float delta[KV_QC];
 };
 
-struct KvSmem {
-  bf16 K[KMAX * 64];  // rows of the problem's keys (B operands of S)
-  bf16 V[KMAX * 64];  // (B operands of dP)
-  KvBuf buf[2];
-};
-
-// One workgroup per (unit, KV head) problem.  The two waves of a SIMD (w and
-// w + 4) hold 5 of the 20 tile slots between them, so the SIMDs stay within
-// one tile of each other even though the waves do not.
+// One workgroup per (unit, KV head) problem.  Each wave keeps the K and V
+// rows of its tiles (the B operands of S and dP) and their dK^T, dV^T
+// accumulators in registers for the whole kernel; only the query rows pass
+// through LDS.  The two waves of a SIMD (w and w + 4) hold 5 of the 20 tile
+// slots between them.
+//
+// Masks are tested on folded row indices r = position * G + head: a key k is
+// visible to row r in time attention iff k*G <= r < (k + W)*G, and a row is
+// an agent row iff agent_begin*G <= r < (agent_begin + agent_count)*G.
+// Keys past the end only feed their own (discarded) dK, dV columns here, so
+// they need no mask.
 template <int OP>
 __global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) KvSmem sm;
-  constexpr int NT = KV_W * 64;
+  __shared__ __attribute__((aligned(16))) KvBuf sbuf[2];
 
   int ug, wg;
   xcd_remap(blockIdx.x, p.units * p.Hkv, 1, ug, wg);
@@ -308,23 +309,37 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
   const int G = p.G;
   const int64_t qhead = (int64_t)g * G * 64;
-  const bf16* kbase = p.k + gk.base + g * 64;
-  const bf16* vbase = p.v + gk.base + g * 64;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
   const int nkt = (p.L + 15) >> 4;
-  const int lp16 = nkt * 16;
 
-  for (int idx = tid; idx < lp16 * 8; idx += NT) {
-    const int r = idx >> 3, c = idx & 7;
-    const bool ok = r < p.L;
-    const bf16x8 kv = ok ? ld_global16(kbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
-    const bf16x8 vv = ok ? ld_global16(vbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
-    st_lds16(sm.K + krow_off(r, c), kv);
-    st_lds16(sm.V + krow_off(r, c), vv);
+  // K and V operands of the wave's tiles, straight from global memory
+  // (keys past the end read as zero)
+  bf16x8 KB[KV_TPW][2], VB[KV_TPW][2];
+  int keyG[KV_TPW];    // time: key * G
+  bool kagent[KV_TPW];  // space: the lane's key is an agent key
+  bool keyok[KV_TPW];
+#pragma unroll
+  for (int m = 0; m < KV_TPW; ++m) {
+    const int key = (wave + KV_W * m) * 16 + li;
+    const bool ok = key < p.L;
+    const int64_t off = gk.base + (int64_t)min(key, p.L - 1) * gk.pos_stride + g * 64;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 kv = ld_global16(p.k + off + (s * 4 + lg) * 8);
+      const bf16x8 vv = ld_global16(p.v + off + (s * 4 + lg) * 8);
+      KB[m][s] = ok ? kv : zero8();
+      VB[m][s] = ok ? vv : zero8();
+    }
+    keyG[m] = key * G;
+    kagent[m] = (unsigned)(key - p.agent_begin) < (unsigned)p.agent_count;
+    keyok[m] = ok;
   }
+  const unsigned winG = p.window > 0 ? (unsigned)(p.window * G) : 0xffffffffu;
+  const int agentG0 = p.agent_begin * G;
+  const unsigned agentGn = (unsigned)(p.agent_count * G);
 
   f32x4 dKT[KV_TPW][4], dVT[KV_TPW][4];
 #pragma unroll
@@ -336,11 +351,11 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     }
 
   // staging: threads 0..255 carry Q (and LSE), threads 256..511 dO (and Delta);
-  // a piece is (row, 16-byte column chunk) of the chunk
+  // a piece is (row, 16-byte column chunk) of the chunk.  The loads are only
+  // issued by fetch(); the LSE transform waits for stage() so that no wave
+  // stalls on a global load a chunk early.
   const bool carries_q = tid < 256;
   const int srow = (tid & 255) >> 3, sch = tid & 7;
-  // The loads are only issued here; the LSE transform waits for stage() so
-  // that no wave stalls on the global load a chunk early.
   bf16x8 pre = zero8();
   float pre_s = 0.f;
   bool pre_valid = false;
@@ -366,109 +381,91 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     }
   };
 
-  // K and V operands of the next slot are read while this one computes, and
-  // those of slot 0 at the end of the previous chunk (a slot past the last
-  // tile reads the last tile and is skipped)
-  auto load_kv = [&](int m, bf16x8* kb, bf16x8* vb) {
-    const int key = min(wave + KV_W * m, nkt - 1) * 16 + li;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      kb[s] = ld_lds16(sm.K + krow_off(key, s * 4 + lg));
-      vb[s] = ld_lds16(sm.V + krow_off(key, s * 4 + lg));
-    }
-  };
-
   const int nchunks = (p.rows + KV_QC - 1) / KV_QC;
   fetch(0);
-  stage(sm.buf[0]);
+  stage(sbuf[0]);
   if (1 < nchunks) fetch(1);
   __syncthreads();
-  bf16x8 KB0[2], VB0[2];
-  load_kv(0, KB0, VB0);
 
   for (int c = 0; c < nchunks; ++c) {
-    KvBuf& b = sm.buf[c & 1];
+    KvBuf& b = sbuf[c & 1];
     const int r0 = c * KV_QC;
     const int qlo = r0 / G;
     const int qhi = (min(r0 + KV_QC, p.rows) - 1) / G;
-    bool work[KV_TPW];
+    const bool world_rows = !(qlo >= p.agent_begin && qhi < p.agent_begin + p.agent_count);
+    bool work[KV_TPW], edge[KV_TPW];
     bool anyw = false;
 #pragma unroll
     for (int m = 0; m < KV_TPW; ++m) {
       const int t = wave + KV_W * m;
-      work[m] = t < nkt && !tile_none_visible(md, qlo, qhi, t * 16, t * 16 + 16);
+      const int k0 = t * 16, k1 = min(t * 16 + 16, p.L);
+      work[m] = t < nkt && !tile_none_visible(md, qlo, qhi, k0, k1);
+      if (OP == OP_TIME)
+        edge[m] = !tile_all_visible(md, qlo, qhi, k0, k1);
+      else
+        edge[m] = world_rows && p.agent_count > 0 && k0 < p.agent_begin + p.agent_count && k1 > p.agent_begin;
       anyw |= work[m];
     }
+    bf16x8 Pb[KV_TPW], dSb[KV_TPW];
     if (anyw) {
-      // 1. S and dP for the owned tiles, then P and dS as packed B operands
-      bf16x8 Pb[KV_TPW], dSb[KV_TPW];
-      {
-        bf16x8 Qa[2][2], dOa[2][2];
+      // 1. S and dP for the owned tiles, then P and dS as packed B operands,
+      // one 16-row half of the chunk at a time
+      bf16x4 Ph[KV_TPW][2], dSh[KV_TPW][2];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < 2; ++qt) {
+        bf16x8 Qa[2], dOa[2];
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            Qa[qt][s] = ld_lds16(b.Q + row_off(qt * 16 + li, s * 4 + lg));
-            dOa[qt][s] = ld_lds16(b.dO + row_off(qt * 16 + li, s * 4 + lg));
-          }
-        f32x4 lse4[2], ndl4[2];
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
-          ndl4[qt] = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
+        for (int s = 0; s < 2; ++s) {
+          Qa[s] = ld_lds16(b.Q + row_off(qt * 16 + li, s * 4 + lg));
+          dOa[s] = ld_lds16(b.dO + row_off(qt * 16 + li, s * 4 + lg));
         }
-        bf16x8 KB[2] = {KB0[0], KB0[1]}, VB[2] = {VB0[0], VB0[1]};
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
+        const f32x4 ndl4 = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
+        const int rb = r0 + qt * 16 + lg * 4;  // folded row of element j = rb + j
 #pragma unroll
         for (int m = 0; m < KV_TPW; ++m) {
-          bf16x8 KBn[2], VBn[2];
-          if (m + 1 < KV_TPW) load_kv(m + 1, KBn, VBn);
-          if (work[m]) {
-          const int kabs = (wave + KV_W * m) * 16;
-          f32x4 S[2], dP[2];
+          if (!work[m]) continue;
+          f32x4 S = {0.f, 0.f, 0.f, 0.f};
+          S = mfma16(Qa[0], KB[m][0], S);
+          S = mfma16(Qa[1], KB[m][1], S);
+          // the accumulator starts at -Delta, so it ends at dP - Delta
+          f32x4 dP = ndl4;
+          dP = mfma16(dOa[0], VB[m][0], dP);
+          dP = mfma16(dOa[1], VB[m][1], dP);
+          f32x4 P;
 #pragma unroll
-          for (int qt = 0; qt < 2; ++qt) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            z = mfma16(Qa[qt][0], KB[0], z);
-            S[qt] = mfma16(Qa[qt][1], KB[1], z);
-            // the accumulator starts at -Delta, so it ends at dP - Delta
-            f32x4 y = ndl4[qt];
-            y = mfma16(dOa[qt][0], VB[0], y);
-            dP[qt] = mfma16(dOa[qt][1], VB[1], y);
+          for (int j = 0; j < 4; ++j) P[j] = fast_exp2(__builtin_fmaf(S[j], p.scale_log2, -lse4[j]));
+          if (edge[m]) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              bool vis;
+              if (OP == OP_TIME)
+                vis = (unsigned)(rb + j - keyG[m]) < winG && rb + j >= keyG[m];
+              else
+                vis = keyok[m] && (!kagent[m] || (unsigned)(rb + j - agentG0) < agentGn);
+              P[j] = vis ? P[j] : 0.f;
+            }
           }
-          f32x4 P[2], dS[2];
-          if (tile_all_visible(md, qlo, qhi, kabs, kabs + 16)) {
+          f32x4 dS;
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
-                P[qt][j] = e;
-                dS[qt][j] = e * dP[qt][j];
-              }
-          } else {
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int qp = row_pos(r0 + qt * 16 + lg * 4 + j, p.inv_g);
-                const bool vis = visible_op<OP>(md, qp, kabs + li);
-                const float e = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
-                const float pv = vis ? e : 0.f;
-                P[qt][j] = pv;
-                dS[qt][j] = pv * dP[qt][j];
-              }
-          }
-          Pb[m] = pack8(P[0], P[1]);
-          dSb[m] = pack8(dS[0], dS[1]);
-          }
-          if (m + 1 < KV_TPW) {
-            KB[0] = KBn[0];
-            KB[1] = KBn[1];
-            VB[0] = VBn[0];
-            VB[1] = VBn[1];
-          }
+          for (int j = 0; j < 4; ++j) dS[j] = P[j] * dP[j];
+          Ph[m][qt] = pack4(P);
+          dSh[m][qt] = pack4(dS);
         }
       }
+#pragma unroll
+      for (int m = 0; m < KV_TPW; ++m) {
+        Pb[m] = join8(Ph[m][0], Ph[m][1]);
+        dSb[m] = join8(dSh[m][0], dSh[m][1]);
+      }
+    }
+    // the next chunk goes into the other buffer (last read before the
+    // previous barrier) while this chunk's second phase runs
+    if (c + 1 < nchunks) {
+      stage(sbuf[(c + 1) & 1]);
+      if (c + 2 < nchunks) fetch(c + 2);
+    }
+    if (anyw) {
       // 2. dV^T += dO^T P and dK^T += Q^T dS; all transposed operands are
       // read first so that one LDS round trip covers the whole phase
       bf16x8 qta[4], dota[4];
@@ -487,13 +484,6 @@ void attn_bwd_dkv_kernel(BwdParams p) {
           dKT[m][dt] = mfma16(qta[dt], dSb[m], dKT[m][dt]);
         }
       }
-    }
-    // next chunk into the other buffer (last read before the previous
-    // barrier), then prefetch the one after
-    load_kv(0, KB0, VB0);
-    if (c + 1 < nchunks) {
-      stage(sm.buf[(c + 1) & 1]);
-      if (c + 2 < nchunks) fetch(c + 2);
     }
     __syncthreads();
   }
@@ -560,7 +550,6 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
   const long g1 = problems * p.splits;
   // dkv kernel: one workgroup per problem (20 tile slots cover 320 keys)
-  p.nwg = 1;
   const long g2 = problems;
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 

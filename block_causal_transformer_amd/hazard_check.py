@@ -1,0 +1,137 @@
+"""Check gfx950 device assembly for MFMA results read too early.
+
+hipcc leaves a number of wait states between an MFMA and the first non-MFMA
+instruction that reads its destination registers (gfx950 does not interlock
+that dependency).  On straight-line code it always leaves at least
+``MIN_STATES``; across a conditional branch that skips a block it has been
+seen to leave only one, so the consumer read the accumulator's old value and
+the kernel returned wrong, run-to-run different results.  This module walks
+every control-flow path after each MFMA (fall-through and branch targets)
+and reports any read of its destination that comes sooner.
+
+    python -m block_causal_transformer_amd.hazard_check FILE.s [...]
+
+``build`` runs it on the assembly of every HIP source and fails on a hit.
+"""
+from __future__ import annotations
+
+import re
+import sys
+
+MIN_STATES = 8
+
+_STORES = ("ds_write", "global_store", "buffer_store", "scratch_store", "flat_store")
+
+
+def _regs(tok: str) -> set:
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.fullmatch(r"([va])(\d+)", tok)
+    if m:
+        return {(m.group(1), int(m.group(2)))}
+    return set()
+
+
+def _parse(lines):
+    ins, labels = [], {}
+    for ln in lines:
+        s = ln.split(";")[0].strip()
+        if not s:
+            continue
+        if s.endswith(":"):
+            labels[s[:-1]] = len(ins)
+            continue
+        if s.startswith("."):
+            continue
+        parts = s.split(None, 1)
+        args = [a.strip() for a in parts[1].split(",")] if len(parts) > 1 else []
+        ins.append((parts[0], args, s))
+    return ins, labels
+
+
+def _kernels(text: str):
+    """(name, lines) of every function body in an assembly file."""
+    out, name, cur = [], None, []
+    for ln in text.split("\n"):
+        m = re.match(r"^([A-Za-z_][\w.$]*):", ln)
+        if m and not ln.startswith(".") and name is None and not m.group(1).startswith(".L"):
+            name, cur = m.group(1), []
+            continue
+        if name is not None:
+            cur.append(ln)
+            if "s_endpgm" in ln:
+                out.append((name, cur))
+                name = None
+    return out
+
+
+def check_function(lines, min_states: int = MIN_STATES):
+    """List of (mfma text, consumer text, wait states) violations."""
+    ins, labels = _parse(lines)
+    bad = []
+    for i, (op, args, text) in enumerate(ins):
+        if not op.startswith("v_mfma") or not args:
+            continue
+        dst = _regs(args[0])
+        stack, seen = [(i + 1, 0)], set()
+        while stack:
+            j, st = stack.pop()
+            if st >= min_states or j >= len(ins) or (j, st) in seen:
+                continue
+            seen.add((j, st))
+            op2, a2, text2 = ins[j]
+            if op2.startswith("v_mfma"):
+                # another MFMA may take the result as an operand (the
+                # hardware forwards it); one that overwrites it ends the hazard
+                if a2 and _regs(a2[0]) & dst:
+                    continue
+            else:
+                srcs = a2 if op2.startswith(_STORES) else a2[1:]
+                used = set()
+                for a in srcs:
+                    used |= _regs(a)
+                if used & dst:
+                    bad.append((text, text2, st))
+            nst = st + (int(a2[0], 0) + 1 if op2 == "s_nop" else 1)
+            if op2 == "s_endpgm":
+                continue
+            if op2 == "s_branch":
+                stack.append((labels[a2[0]], nst))
+                continue
+            if op2.startswith("s_cbranch"):
+                stack.append((labels[a2[0]], nst))
+            stack.append((j + 1, nst))
+    return bad
+
+
+def check_text(text: str, min_states: int = MIN_STATES):
+    """{kernel: violations} for every kernel with at least one."""
+    res = {}
+    for name, lines in _kernels(text):
+        bad = check_function(lines, min_states)
+        if bad:
+            res[name] = bad
+    return res
+
+
+def check_file(path: str, min_states: int = MIN_STATES):
+    with open(path) as f:
+        return check_text(f.read(), min_states)
+
+
+def main(argv=None):
+    argv = sys.argv[1:] if argv is None else argv
+    status = 0
+    for path in argv:
+        res = check_file(path)
+        for name, bad in res.items():
+            status = 1
+            print("%s: %s: %d MFMA result read(s) within %d wait states" % (path, name, len(bad), MIN_STATES))
+            for mf, use, st in bad[:5]:
+                print("    %s  ->  %s  (after %d)" % (mf, use, st))
+    return status
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,57 @@
+"""The device-assembly check for MFMA results read too early
+(block_causal_transformer_amd.hazard_check), on hand-written snippets and on
+the assembly of the built kernels."""
+import glob
+import os
+
+import pytest
+
+from block_causal_transformer_amd import hazard_check as H
+
+HEAD = """k:
+\tv_mfma_f32_16x16x32_bf16 v[4:7], v[0:3], v[8:11], v[4:7]
+\ts_cbranch_vccnz .LBB0_2
+\tv_add_u32_e32 v20, 1, v21
+\tv_add_u32_e32 v20, 1, v21
+\tv_add_u32_e32 v20, 1, v21
+\ts_nop 6
+.LBB0_2:
+"""
+TAIL = """\tv_mul_f32_e32 v4, v12, v4
+\ts_endpgm
+"""
+
+
+def test_read_after_skipped_block_is_flagged():
+    bad = H.check_text(HEAD + TAIL)
+    assert "k" in bad and bad["k"][0][2] == 1, bad
+
+
+def test_enough_wait_states_on_every_path_pass():
+    assert H.check_text(HEAD + "\ts_nop 7\n" + TAIL) == {}
+
+
+def test_unrelated_registers_and_store_sources():
+    text = HEAD.replace("s_nop 6", "s_nop 0") + "\tv_mul_f32_e32 v30, v12, v31\n\tds_write_b128 v40, v[4:7]\n\ts_endpgm\n"
+    bad = H.check_text(text)
+    assert "k" in bad and "ds_write_b128" in bad["k"][0][1]
+
+
+def test_mfma_chain_is_not_a_hazard():
+    text = """k:
+\tv_mfma_f32_16x16x32_bf16 v[4:7], v[0:3], v[8:11], 0
+\tv_mfma_f32_16x16x32_bf16 v[4:7], v[12:15], v[16:19], v[4:7]
+\ts_nop 7
+\tv_mul_f32_e32 v4, v12, v4
+\ts_endpgm
+"""
+    assert H.check_text(text) == {}
+
+
+def test_built_kernels_pass():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    files = glob.glob(os.path.join(root, "_build", "asm", "*.s"))
+    if not files:
+        pytest.skip("no device assembly built")
+    for f in files:
+        assert H.check_file(f) == {}, f
