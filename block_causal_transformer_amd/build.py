@@ -25,6 +25,10 @@ SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_generic.hip", "bca_abi.cpp"]
 ARCH = os.environ.get("BCA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+# per-source device scheduling: the backward kernels interleave better with
+# the scheduler's maximum-ILP strategy (measured ~5% on the dK/dV kernel)
+EXTRA = {"attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -33,11 +37,11 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
 
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", out]
     if src.startswith("asm:"):
         src = src[4:]
         out = os.path.join(ASM, os.path.splitext(src)[0] + ".s")
-        cmd = [HIPCC] + COMMON + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+        cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = ("is not a recognized feature for this target", "argument unused during compilation: '--hip-link'")
     err = "\n".join(l for l in r.stderr.splitlines() if not any(n in l for n in noise))

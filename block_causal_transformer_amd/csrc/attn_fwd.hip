@@ -97,14 +97,28 @@ void attn_fwd_kernel(FwdParams p) {
   const int passes = (nch + FW - 1) / FW;
   const int G = p.G;
 
+  // this lane's query column in each 16-column tile of a chunk; padding
+  // columns read a real (clamped) row and are never stored.  The next
+  // chunk's Q is loaded before this chunk's O is stored, so that the first
+  // products of the next chunk do not wait behind the stores.
+  bf16x8 qreg[NQT][2];
+  auto load_q = [&](int pass) {
+    const int r0n = row0 + (pass * FW + wave) * QCH;
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int rr = min(r0n + qt * 16 + li, row1 - 1);
+      const int pos = row_pos(rr, p.inv_g);
+      const bf16* src = qbase + pos * gq.pos_stride + (rr - pos * G) * 64 + lg * 8;
+      qreg[qt][0] = ld_global16(src);
+      qreg[qt][1] = ld_global16(src + 32);
+    }
+  };
+  if (wave < nch) load_q(0);
   for (int pass = 0; pass < passes; ++pass) {
     const int ch = pass * FW + wave;
     const bool active = ch < nch;
     const int r0 = row0 + ch * QCH;
 
-    // this lane's query column in each 16-column tile; padding columns read
-    // a real (clamped) row and are never stored
-    bf16x8 qreg[NQT][2];
     int qpos[NQT], hh[NQT];
     bool qvalid[NQT];
     f32x4 acc[NQT][4];
@@ -118,9 +132,6 @@ void attn_fwd_kernel(FwdParams p) {
         const int rr = min(r, row1 - 1);
         qpos[qt] = row_pos(rr, p.inv_g);
         hh[qt] = rr - qpos[qt] * G;
-        const bf16* src = qbase + qpos[qt] * gq.pos_stride + hh[qt] * 64 + lg * 8;
-        qreg[qt][0] = ld_global16(src);
-        qreg[qt][1] = ld_global16(src + 32);
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[qt] = -INFINITY;
@@ -192,22 +203,24 @@ void attn_fwd_kernel(FwdParams p) {
         // reference moves only when one of its scores exceeds it by more
         // than 2^8, and only that row is rescaled (the others multiply by
         // exactly 1), so every row depends on its own scores alone
-        float mx[NQT];
-        bool grow[NQT];
-        bool any = false;
+        // each lane first tests its own 8 scores of the row; the 4-lane
+        // row maximum is formed only when some lane of the wave is over
+        float lmx[NQT];
+        bool over = false;
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
           const float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
           const float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
-          mx[qt] = group4_max(fmaxf(a, b)) * p.scale_log2;
-          grow[qt] = mx[qt] > m[qt] + kRescaleThreshold;
-          any |= grow[qt];
+          lmx[qt] = fmaxf(a, b) * p.scale_log2;
+          over |= lmx[qt] > m[qt] + kRescaleThreshold;
         }
-        if (__builtin_amdgcn_ballot_w64(any)) {
+        if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
           for (int qt = 0; qt < NQT; ++qt) {
-            const float mn = grow[qt] ? mx[qt] : m[qt];
-            const float alpha = grow[qt] ? fast_exp2(m[qt] - mn) : 1.f;
+            const float mx = group4_max(lmx[qt]);
+            const bool grow = mx > m[qt] + kRescaleThreshold;
+            const float mn = grow ? mx : m[qt];
+            const float alpha = grow ? fast_exp2(m[qt] - mn) : 1.f;
             l[qt] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc[qt][dt] *= alpha;
@@ -238,6 +251,7 @@ void attn_fwd_kernel(FwdParams p) {
     }
 
     if (active) {
+      if (ch + FW < nch) load_q(pass + 1);
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) {
         const float lt = group4_sum(l[qt]);
