@@ -271,6 +271,67 @@ int oracle_time_bwd(int B, int T, int N, int Hq, int Hkv, int D, int window, dou
   return attn_bwd(1, B, T, N, Hq, Hkv, D, window, 0, 0, scale, q, k, v, dout, dq, dk, dv);
 }
 
+/* Rollout decode of time attention.  Open Dreamer articles (pro.edgex.exchange,
+ * fr-FR edition), section "Artefacts publiés": the pipeline ships rollout
+ * generation and a local rollout harness, and the browser demo streams the
+ * generated world frame by frame; section "Architecture": time layers are
+ * causal across frames.  Reading: generating frame a runs the same time
+ * attention as training, restricted to the query rows of the new frames, with
+ * the keys and values of earlier frames taken from a cache.
+ *
+ * The queries are Tq consecutive frames with absolute indices q_frame0 ..
+ * q_frame0 + Tq - 1: q, o are (B,Tq,N,Hq,D), lse (B,Tq,N,Hq).  The cache kc,
+ * vc is (B,C,N,Hkv,D) and holds absolute frame f at ring position f % C.
+ * Query frame a sees frame f iff f <= a and (W == 0 or a - f <= W - 1), the
+ * predicate of oracle_time_fwd.  Every frame some query sees must be in the
+ * ring: (last query frame) - (first visible frame) + 1 <= C. */
+int oracle_time_decode_fwd(int B, int Tq, int N, int Hq, int Hkv, int D, int window,
+                           double scale, int C, int q_frame0, const double* q,
+                           const double* kc, const double* vc, double* o, double* lse) {
+  if (check_shape(B, Tq, N, Hq, Hkv, D) || window < 0 || C <= 0 || q_frame0 < 0) return -1;
+  const int last = q_frame0 + Tq - 1;
+  const int first = (window > 0 && q_frame0 - window + 1 > 0) ? q_frame0 - window + 1 : 0;
+  if (last - first + 1 > C) return -1;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+  const int G = Hq / Hkv;
+  problem P;
+  P.is_time = 1;
+  P.window = window;
+  P.agent_begin = 0;
+  P.agent_count = 0;
+  P.L = last + 1;
+#pragma omp parallel for schedule(dynamic)
+  for (long job = 0; job < (long)B * N * Hq; ++job) {
+    const int h = (int)(job % Hq), g = h / G;
+    const int n = (int)((job / Hq) % N), b = (int)(job / ((long)Hq * N));
+    double* z = (double*)malloc(sizeof(double) * (last + 1));
+    for (int t = 0; t < Tq; ++t) {
+      const int a = q_frame0 + t;
+      const long qo = (((long)b * Tq + t) * N + n) * Hq * D + (long)h * D;
+      double m = -INFINITY;
+      for (int f = 0; f <= last; ++f) {
+        if (!visible(&P, a, f)) continue;
+        const long ko = (((long)b * C + f % C) * N + n) * Hkv * D + (long)g * D;
+        z[f] = scale * dot(q + qo, kc + ko, D);
+        if (z[f] > m) m = z[f];
+      }
+      double l = 0.0;
+      for (int d = 0; d < D; ++d) o[qo + d] = 0.0;
+      for (int f = 0; f <= last; ++f) {
+        if (!visible(&P, a, f)) continue;
+        const long vo = (((long)b * C + f % C) * N + n) * Hkv * D + (long)g * D;
+        const double e = exp(z[f] - m);
+        l += e;
+        for (int d = 0; d < D; ++d) o[qo + d] += e * vc[vo + d];
+      }
+      for (int d = 0; d < D; ++d) o[qo + d] /= l;
+      lse[(((long)b * Tq + t) * N + n) * Hq + h] = m + log(l);
+    }
+    free(z);
+  }
+  return 0;
+}
+
 void oracle_set_threads(int n) {
 #ifdef _OPENMP
   if (n > 0) omp_set_num_threads(n);

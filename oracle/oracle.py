@@ -45,7 +45,9 @@ def _declare(h: ctypes.CDLL) -> ctypes.CDLL:
     h.oracle_space_bwd.argtypes = [i] * 6 + [i, i, d] + [_DP] * 7
     h.oracle_time_fwd.argtypes = [i] * 6 + [i, d] + [_DP] * 5
     h.oracle_time_bwd.argtypes = [i] * 6 + [i, d] + [_DP] * 7
-    for f in (h.oracle_space_fwd, h.oracle_space_bwd, h.oracle_time_fwd, h.oracle_time_bwd):
+    h.oracle_time_decode_fwd.argtypes = [i] * 7 + [d, i, i] + [_DP] * 5
+    for f in (h.oracle_space_fwd, h.oracle_space_bwd, h.oracle_time_fwd, h.oracle_time_bwd,
+              h.oracle_time_decode_fwd):
         f.restype = ctypes.c_int
     h.oracle_set_threads.argtypes = [i]
     h.oracle_set_threads.restype = None
@@ -149,6 +151,24 @@ def time_bwd(q, k, v, dout, window: int = 0, scale: float = 0.0,
     _check(h.oracle_time_bwd(B, T, N, Hq, Hkv, D, window, scale,
                              _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv)), "time_bwd")
     return dq, dk, dv
+
+
+def time_decode_fwd(q, kc, vc, q_frame0: int, window: int = 0, scale: float = 0.0,
+                    lib: Optional[ctypes.CDLL] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Rollout decode of time attention: queries are the frames q_frame0 ..
+    q_frame0 + Tq - 1 (q is (B,Tq,N,Hq,D)); kc, vc (B,C,N,Hkv,D) hold absolute
+    frame f at ring position f % C.  Returns (o, lse) in float64."""
+    h = lib or load()
+    q, kc, vc = _f64(q), _f64(kc), _f64(vc)
+    B, Tq, N, Hq, D = q.shape
+    C, Hkv = kc.shape[1], kc.shape[3]
+    if kc.shape != (B, C, N, Hkv, D) or vc.shape != kc.shape:
+        raise ValueError("cache shape %s does not match q shape %s" % (kc.shape, q.shape))
+    o = np.zeros_like(q)
+    lse = np.zeros((B, Tq, N, Hq))
+    _check(h.oracle_time_decode_fwd(B, Tq, N, Hq, Hkv, D, window, scale, C, q_frame0,
+                                    _p(q), _p(kc), _p(vc), _p(o), _p(lse)), "time_decode_fwd")
+    return o, lse
 
 
 def fwd(w, q, k, v, scale: float = 0.0, lib=None):

@@ -14,7 +14,10 @@ disagrees with what the mathematics or the pages fix:
 * invariants: future / out-of-window frames and agent keys do not reach the
   outputs they may not reach; GQA equals replicated KV heads; a common key
   shift leaves O unchanged and shifts LSE by s<q, c>; permuting world tokens
-  permutes outputs; units are independent.
+  permutes outputs; units are independent;
+* rollout decode: torch SDPA over the ring positions with a mask built from
+  the frame each position holds, and row t of time attention over the whole
+  sequence.
 """
 from __future__ import annotations
 
@@ -407,9 +410,90 @@ def pin_units_independent(lib):
         close(lse2, S(lse), 1e-13, "units lse " + op)
 
 
+# ------------------------------------------------------- rollout decode
+
+def ring_frames(C, last):
+    """Absolute frame held by each ring position after frames up to ``last``
+    were written at f % C (-1: never written)."""
+    out = np.full(C, -1)
+    for f in range(max(0, last - C + 1), last + 1):
+        out[f % C] = f
+    return out
+
+
+# (B, Tq, N, Hq, Hkv, D, W, C, q_frame0)
+DECODE_CASES = [
+    (1, 1, 3, 4, 2, 8, 4, 4, 10),   # steady state, ring wrapped, C = W
+    (2, 1, 2, 3, 1, 5, 3, 5, 1),    # second frame: partial history, C > W
+    (1, 3, 2, 2, 2, 4, 0, 7, 4),    # unbounded window, three new frames fill the ring
+    (1, 2, 2, 6, 3, 3, 5, 6, 20),   # two new frames, C = W + 1
+    (1, 1, 2, 4, 2, 16, 1, 3, 7),   # window 1
+]
+
+
+def decode_ref(q, kc, vc, q_frame0, W, scale=0.0):
+    """torch fp64 SDPA over the ring positions, masked by which frame each
+    position holds; LSE from torch.logsumexp."""
+    B, Tq, N, Hq, D = q.shape
+    C, Hkv = kc.shape[1], kc.shape[3]
+    s = scale if scale > 0 else 1.0 / math.sqrt(D)
+    held = ring_frames(C, q_frame0 + Tq - 1)
+    a = (q_frame0 + np.arange(Tq))[:, None]
+    f = held[None, :]
+    m = (f >= 0) & (f <= a)
+    if W > 0:
+        m &= (a - f) <= W - 1
+    mt = torch.tensor(m)
+    qt = torch.tensor(q.transpose(0, 2, 3, 1, 4).reshape(B * N, Hq, Tq, D))
+    kt = torch.tensor(kc.transpose(0, 2, 3, 1, 4).reshape(B * N, Hkv, C, D))
+    vt = torch.tensor(vc.transpose(0, 2, 3, 1, 4).reshape(B * N, Hkv, C, D))
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt, scale=s, enable_gqa=(Hq != Hkv))
+    kr = kt.repeat_interleave(Hq // Hkv, dim=1)
+    z = (torch.matmul(qt, kr.transpose(-1, -2).contiguous()) * s).masked_fill(~mt, float("-inf"))
+    lse = torch.logsumexp(z, dim=-1)
+    o = o.numpy().reshape(B, N, Hq, Tq, D).transpose(0, 3, 1, 2, 4)
+    lse = lse.numpy().reshape(B, N, Hq, Tq).transpose(0, 3, 1, 2)
+    return o, lse
+
+
+def pin_decode_sdpa(lib):
+    """Decode against a library routine over the ring positions."""
+    for i, (B, Tq, N, Hq, Hkv, D, W, C, t0) in enumerate(DECODE_CASES):
+        q = rnd((B, Tq, N, Hq, D), 510 + i)
+        kc = rnd((B, C, N, Hkv, D), 520 + i)
+        vc = rnd((B, C, N, Hkv, D), 530 + i)
+        sc = 0.0 if i % 2 == 0 else 0.41
+        o, lse = O.time_decode_fwd(q, kc, vc, t0, W, sc, lib=lib)
+        ro, rl = decode_ref(q, kc, vc, t0, W, sc)
+        close(o, ro, 1e-10, "decode case %d o" % i)
+        close(lse, rl, 1e-10, "decode case %d lse" % i)
+
+
+def pin_decode_matches_full_sequence(lib):
+    """Decoding frame t from a ring filled with frames <= t reproduces row t
+    of time attention over the whole sequence (the training op)."""
+    B, T, N, Hq, Hkv, D = 1, 11, 3, 4, 2, 8
+    q = rnd((B, T, N, Hq, D), 541)
+    k = rnd((B, T, N, Hkv, D), 542)
+    v = rnd((B, T, N, Hkv, D), 543)
+    for W, C in ((4, 4), (4, 6), (0, 11)):
+        o_full, lse_full = O.time_fwd(q, k, v, W, lib=lib)
+        for t in (0, 2, 5, 10):
+            held = ring_frames(C, t)
+            kc = np.zeros((B, C, N, Hkv, D))
+            vc = np.zeros((B, C, N, Hkv, D))
+            for pos, f in enumerate(held):
+                if f >= 0:
+                    kc[:, pos], vc[:, pos] = k[:, f], v[:, f]
+            o, lse = O.time_decode_fwd(q[:, t:t + 1], kc, vc, t, W, lib=lib)
+            close(o[:, 0], o_full[:, t], 1e-12, "decode vs full o W=%d C=%d t=%d" % (W, C, t))
+            close(lse[:, 0], lse_full[:, t], 1e-12, "decode vs full lse W=%d C=%d t=%d" % (W, C, t))
+
+
 ALL_PINS = [
     pin_sdpa_space, pin_sdpa_time, pin_identical_keys, pin_q_zero_golden, pin_window_one,
     pin_constant_values, pin_backward_sums, pin_finite_differences,
     pin_future_and_window_invariance, pin_agent_invariance, pin_gqa_equals_replicated,
     pin_key_shift, pin_permute_world_tokens, pin_units_independent,
+    pin_decode_sdpa, pin_decode_matches_full_sequence,
 ]

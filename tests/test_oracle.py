@@ -50,6 +50,13 @@ MUTANTS = [
     ("space_unit_base", "*kv0 = (long)u * N * Hkv * D;", "*kv0 = (long)(u % 2) * N * Hkv * D;"),
     ("fwd_p_unnormalised", "for (int b = 0; b < P->L; ++b) p[b] /= l;",
      "for (int b = 0; b < P->L; ++b) p[b] /= (l + 1e-3);"),
+    ("decode_ring_key", "const long ko = (((long)b * C + f % C) * N + n) * Hkv * D + (long)g * D;",
+     "const long ko = (((long)b * C + (f + 1) % C) * N + n) * Hkv * D + (long)g * D;"),
+    ("decode_ring_value", "const long vo = (((long)b * C + f % C) * N + n) * Hkv * D + (long)g * D;",
+     "const long vo = (((long)b * C + f / C) * N + n) * Hkv * D + (long)g * D;"),
+    ("decode_query_frame", "const int a = q_frame0 + t;", "const int a = q_frame0 + t + 1;"),
+    ("decode_lse", "lse[(((long)b * Tq + t) * N + n) * Hq + h] = m + log(l);",
+     "lse[(((long)b * Tq + t) * N + n) * Hq + h] = log(l);"),
 ]
 
 
