@@ -156,3 +156,77 @@ BENCH_STEP: List[str] = ["3", "4"]
 
 def get(name: str) -> Workload:
     return CONFIGS[name]
+
+
+# ------------------------------------------------------------ rollout decode
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Time attention of Tq new frames against a ring-buffer K/V cache of C
+    frames (absolute frame f at ring position f % C); the queries are the
+    absolute frames q_frame0 .. q_frame0 + Tq - 1."""
+    name: str
+    B: int
+    Tq: int
+    N: int
+    Hq: int
+    Hkv: int
+    D: int
+    window: int
+    cache_frames: int
+    q_frame0: int
+    dtype: str = "bf16"
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def q_shape(self):
+        return (self.B, self.Tq, self.N, self.Hq, self.D)
+
+    def cache_shape(self):
+        return (self.B, self.cache_frames, self.N, self.Hkv, self.D)
+
+    def key_frames(self) -> Tuple[int, int]:
+        """Absolute frames [first, last] the queries read."""
+        last = self.q_frame0 + self.Tq - 1
+        first = max(0, self.q_frame0 - self.window + 1) if self.window > 0 else 0
+        return first, last
+
+    def with_(self, **kw) -> "DecodeWorkload":
+        return replace(self, **kw)
+
+
+def decode_visible_pairs(w: DecodeWorkload) -> int:
+    per = 0
+    for t in range(w.Tq):
+        a = w.q_frame0 + t
+        per += min(a + 1, w.window) if w.window > 0 else a + 1
+    return per * w.B * w.N * w.Hq
+
+
+def decode_flops(w: DecodeWorkload) -> float:
+    """4*D per visible pair (QK^T and PV)."""
+    return float(4 * w.D * decode_visible_pairs(w))
+
+
+def decode_min_bytes(w: DecodeWorkload) -> float:
+    """Read Q and the cached K, V frames the queries see; write O and LSE."""
+    es = 2 if w.dtype == "bf16" else 4
+    first, last = w.key_frames()
+    nq = w.B * w.Tq * w.N * w.Hq * w.D
+    nkv = w.B * (last - first + 1) * w.N * w.Hkv * w.D
+    return float(es * (2 * nq + 2 * nkv) + 4 * w.B * w.Tq * w.N * w.Hq)
+
+
+# Rollout of the Minecraft dynamics model (frame-by-frame generation, section
+# "Artefacts publiés"): one new frame of 290 slots, 30 / 3 heads, window 192,
+# the ring holding the 192 frames the window reads, steady state (wrapped).
+DECODE_CONFIGS: Dict[str, DecodeWorkload] = {
+    "dec": DecodeWorkload("dec", 1, 1, 290, 30, 3, 64, 192, 192, 1000, "bf16", 6000,
+                          note="Minecraft rollout: one new frame, steady state"),
+    "dec_b8": DecodeWorkload("dec_b8", 8, 1, 290, 30, 3, 64, 192, 192, 1000, "bf16", 6001,
+                             note="Minecraft rollout, 8 environments"),
+}

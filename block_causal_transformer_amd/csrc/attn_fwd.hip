@@ -48,6 +48,10 @@ struct FwdParams {
   int window, agent_begin, agent_count;
   float scale_log2, inv_g;
   int splits, rows_per_split;
+  // decode: K/V hold Tk frames per slot; kernel key position x is absolute
+  // frame kfirst + x at frame (kfirst + x) % Tk; kernel query position y sits
+  // at key position y + qoff
+  int Tk, kfirst, qoff;
 };
 
 // V^T is stored with keys permuted inside each group of 32 so that the 8 keys
@@ -66,7 +70,9 @@ __device__ __forceinline__ int vt_off(int d, int pos) {  // sVT: [64][KMAX]
 }
 
 // 8 waves of 32 query rows; two workgroups (80 KB of LDS each) share a CU,
-// so each SIMD interleaves four waves.
+// so each SIMD interleaves four waves.  OP_DECODE runs the time op's code
+// with the query positions shifted by qoff and the key frames read from a
+// ring (rollout over a KV cache).
 template <int OP>
 __global__ __attribute__((amdgpu_flat_work_group_size(FW * 64, FW * 64), amdgpu_waves_per_eu(4, 4)))
 void attn_fwd_kernel(FwdParams p) {
@@ -77,10 +83,13 @@ void attn_fwd_kernel(FwdParams p) {
   int ug, split;
   xcd_remap(blockIdx.x, p.units * p.Hkv, p.splits, ug, split);
   const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
-  const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, 64);
-  const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
-  const UnitGeom gl = unit_geom(OP, u, p.T, p.N, p.Hq, 1);
-  const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
+  constexpr int MOP = OP == OP_DECODE ? OP_TIME : OP;  // mask and layout kind
+  const int qsh = OP == OP_DECODE ? p.qoff : 0;        // query -> key position
+  const UnitGeom gq = unit_geom(MOP, u, p.T, p.N, p.Hq, 64);
+  const UnitGeom gk = unit_geom(MOP, u, p.Tk, p.N, p.Hkv, 64);
+  const UnitGeom gl = unit_geom(MOP, u, p.T, p.N, p.Hq, 1);
+  const MaskDesc md{MOP, p.L, p.window, p.agent_begin, p.agent_count};
+  auto kframe = [&](int x) { return OP == OP_DECODE ? (p.kfirst + x) % p.Tk : x; };
   const bf16* kbase = p.k + gk.base + g * 64;
   const bf16* vbase = p.v + gk.base + g * 64;
   const bf16* qbase = p.q + gq.base + (int64_t)g * p.G * 64;
@@ -137,8 +146,8 @@ void attn_fwd_kernel(FwdParams p) {
         m[qt] = -INFINITY;
         l[qt] = 0.f;
       }
-      qlo = r0 / G;
-      qhi = (min(r0 + QCH, row1) - 1) / G;
+      qlo = r0 / G + qsh;
+      qhi = (min(r0 + QCH, row1) - 1) / G + qsh;
     }
 
     for (int kb = 0; kb < nkb; ++kb) {
@@ -151,8 +160,8 @@ void attn_fwd_kernel(FwdParams p) {
           const int r = idx >> 3, c = idx & 7;
           bf16x8 kv = zero8(), vv = zero8();
           if (r < kn) {
-            kv = ld_global16(kbase + (int64_t)(key0 + r) * gk.pos_stride + c * 8);
-            vv = ld_global16(vbase + (int64_t)(key0 + r) * gk.pos_stride + c * 8);
+            kv = ld_global16(kbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
+            vv = ld_global16(vbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
           }
           st_lds16(sK + k_off(r, c), kv);
           const int pp = vt_perm(r);
@@ -194,7 +203,7 @@ void attn_fwd_kernel(FwdParams p) {
             for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const bool vis = visible_op<OP>(md, qpos[qt], kabs + h * 16 + lg * 4 + j);
+                const bool vis = visible_op<MOP>(md, qpos[qt] + qsh, kabs + h * 16 + lg * 4 + j);
                 const float cur = sc[qt][h][j];
                 sc[qt][h][j] = vis ? cur : -INFINITY;
               }
@@ -287,6 +296,18 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.L = d.op == OP_SPACE ? d.N : d.T;
   p.units = d.op == OP_SPACE ? d.B * d.T : d.B * d.N;
   p.rows = p.L * p.G;
+  p.Tk = d.T;
+  p.kfirst = 0;
+  p.qoff = 0;
+  if (d.op == OP_DECODE) {
+    int first, last;
+    decode_key_range(d, first, last);
+    p.L = last - first + 1;
+    p.rows = d.T * p.G;
+    p.Tk = d.kv_frames;
+    p.kfirst = first;
+    p.qoff = d.q_frame0 - first;
+  }
   p.window = d.window;
   p.agent_begin = d.agent_begin;
   p.agent_count = d.agent_count;
@@ -307,8 +328,10 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
   if (d.op == OP_SPACE)
     hipLaunchKernelGGL(attn_fwd_kernel<OP_SPACE>, dim3((unsigned)grid), dim3(FW * 64), 0, stream, p);
-  else
+  else if (d.op == OP_TIME)
     hipLaunchKernelGGL(attn_fwd_kernel<OP_TIME>, dim3((unsigned)grid), dim3(FW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<OP_DECODE>, dim3((unsigned)grid), dim3(FW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

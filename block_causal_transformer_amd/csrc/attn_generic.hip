@@ -37,6 +37,11 @@ struct GenParams {
   int op, T, N, Hq, Hkv, G, L, units;
   int window, agent_begin, agent_count;
   float scale;
+  // forward of the decode op: Lq query positions, each at key position
+  // a + qoff; key position b is absolute frame kfirst + b, stored at frame
+  // (kfirst + b) % Tk of k and v.  Plain ops: Lq = L, qoff = kfirst = 0,
+  // Tk = T.
+  int Lq, qoff, kfirst, Tk;
 };
 
 template <typename E>
@@ -52,28 +57,33 @@ __device__ __forceinline__ void stf(E* p, int64_t i, float x) {
 template <typename E, int D>
 __global__ __launch_bounds__(128) void gen_fwd_kernel(GenParams p) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)p.units * p.L * p.Hq;
+  const int64_t total = (int64_t)p.units * p.Lq * p.Hq;
   if (gid >= total) return;
   const int h = (int)(gid % p.Hq);
-  const int a = (int)((gid / p.Hq) % p.L);
-  const int u = (int)(gid / ((int64_t)p.Hq * p.L));
+  const int a = (int)((gid / p.Hq) % p.Lq);
+  const int u = (int)(gid / ((int64_t)p.Hq * p.Lq));
   const int g = h / p.G;
-  const UnitGeom gq = unit_geom(p.op, u, p.T, p.N, p.Hq, D);
-  const UnitGeom gk = unit_geom(p.op, u, p.T, p.N, p.Hkv, D);
-  const UnitGeom gl = unit_geom(p.op, u, p.T, p.N, p.Hq, 1);
-  const MaskDesc md{p.op, p.L, p.window, p.agent_begin, p.agent_count};
+  const int mop = p.op == OP_DECODE ? OP_TIME : p.op;
+  const UnitGeom gq = unit_geom(mop, u, p.T, p.N, p.Hq, D);
+  const UnitGeom gk = unit_geom(mop, u, p.Tk, p.N, p.Hkv, D);
+  const UnitGeom gl = unit_geom(mop, u, p.T, p.N, p.Hq, 1);
+  const MaskDesc md{mop, p.L, p.window, p.agent_begin, p.agent_count};
+  const int ak = a + p.qoff;  // query position among the keys
   const E* q = static_cast<const E*>(p.q) + gq.base + (int64_t)a * gq.pos_stride + (int64_t)h * D;
   const E* k = static_cast<const E*>(p.k) + gk.base + (int64_t)g * D;
   const E* v = static_cast<const E*>(p.v) + gk.base + (int64_t)g * D;
+  auto kpos = [&](int b) -> int64_t {
+    return (int64_t)(p.op == OP_DECODE ? (p.kfirst + b) % p.Tk : b) * gk.pos_stride;
+  };
   float qr[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) qr[d] = ldf(q, d);
   float m = -INFINITY;
   for (int b = 0; b < p.L; ++b) {
-    if (!visible(md, a, b)) continue;
+    if (!visible(md, ak, b)) continue;
     float s = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) s = __builtin_fmaf(qr[d], ldf(k + (int64_t)b * gk.pos_stride, d), s);
+    for (int d = 0; d < D; ++d) s = __builtin_fmaf(qr[d], ldf(k + kpos(b), d), s);
     m = fmaxf(m, s * p.scale);
   }
   float l = 0.f;
@@ -81,14 +91,14 @@ __global__ __launch_bounds__(128) void gen_fwd_kernel(GenParams p) {
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
   for (int b = 0; b < p.L; ++b) {
-    if (!visible(md, a, b)) continue;
+    if (!visible(md, ak, b)) continue;
     float s = 0.f;
 #pragma unroll
-    for (int d = 0; d < D; ++d) s = __builtin_fmaf(qr[d], ldf(k + (int64_t)b * gk.pos_stride, d), s);
+    for (int d = 0; d < D; ++d) s = __builtin_fmaf(qr[d], ldf(k + kpos(b), d), s);
     const float e = expf(s * p.scale - m);
     l += e;
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(e, ldf(v + (int64_t)b * gk.pos_stride, d), acc[d]);
+    for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(e, ldf(v + kpos(b), d), acc[d]);
   }
   E* o = static_cast<E*>(p.out0) + gq.base + (int64_t)a * gq.pos_stride + (int64_t)h * D;
   const float inv = 1.f / l;
@@ -216,12 +226,25 @@ GenParams make_params(const AttnDims& d) {
   p.agent_begin = d.agent_begin;
   p.agent_count = d.agent_count;
   p.scale = d.scale;
+  p.Lq = p.L;
+  p.qoff = 0;
+  p.kfirst = 0;
+  p.Tk = d.T;
+  if (d.op == OP_DECODE) {
+    int first, last;
+    decode_key_range(d, first, last);
+    p.L = last - first + 1;
+    p.Lq = d.T;
+    p.qoff = d.q_frame0 - first;
+    p.kfirst = first;
+    p.Tk = d.kv_frames;
+  }
   return p;
 }
 
 template <typename E, int D>
 hipError_t run_fwd(GenParams p, hipStream_t s) {
-  const int64_t total = (int64_t)p.units * p.L * p.Hq;
+  const int64_t total = (int64_t)p.units * p.Lq * p.Hq;
   const int64_t blocks = (total + 127) / 128;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gen_fwd_kernel<E, D>), dim3((unsigned)blocks), dim3(128), 0, s, p);

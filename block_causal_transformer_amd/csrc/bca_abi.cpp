@@ -137,9 +137,48 @@ int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
   return st;
 }
 
+int do_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* kc,
+                  const void* vc, int32_t cache_frames, int32_t q_frame0, void* o, float* lse,
+                  void* stream) {
+  bca::AttnDims d;
+  int st = validate(BCA_OP_TIME, shape, mask, &d);
+  if (st) return st;
+  const char* names[] = {"q", "k_cache", "v_cache", "o", "lse"};
+  const void* ptrs[] = {q, kc, vc, o, lse};
+  st = check_ptrs(names, ptrs, 5);
+  if (st) return st;
+  if (cache_frames <= 0) return fail(BCA_ERR_INVALID_ARG, "cache_frames %d <= 0", cache_frames);
+  if (q_frame0 < 0) return fail(BCA_ERR_INVALID_ARG, "q_frame0 %d < 0", q_frame0);
+  if ((int64_t)q_frame0 + shape->T - 1 > INT32_MAX)
+    return fail(BCA_ERR_INVALID_ARG, "q_frame0 + T overflows the frame index");
+  if ((double)shape->B * cache_frames * shape->N * shape->Hkv * shape->D > 4.0e15)
+    return fail(BCA_ERR_INVALID_ARG, "cache too large");
+  d.op = bca::OP_DECODE_ID;
+  d.kv_frames = cache_frames;
+  d.q_frame0 = q_frame0;
+  int first, last;
+  bca::decode_key_range(d, first, last);
+  if (last - first + 1 > cache_frames)
+    return fail(BCA_ERR_INVALID_ARG,
+                "a cache of %d frames cannot hold the %d frames [%d, %d] the queries read",
+                cache_frames, last - first + 1, first, last);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = bca::fwd_uses_mfma(d) ? bca::launch_attn_fwd_bf16(d, q, kc, vc, o, lse, s)
+                                       : bca::launch_attn_fwd_generic(d, q, kc, vc, o, lse, s);
+  st = hip_status(e, "time_attn_decode_fwd launch");
+  if (st == BCA_OK) g_last_error.clear();
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
+
+int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q,
+                         const void* k_cache, const void* v_cache, int32_t cache_frames,
+                         int32_t q_frame0, void* o, float* lse, void* stream) {
+  return do_decode_fwd(shape, mask, q, k_cache, v_cache, cache_frames, q_frame0, o, lse, stream);
+}
 
 int space_attn_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
                    const void* v, void* o, float* lse, void* stream) {

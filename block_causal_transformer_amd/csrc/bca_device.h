@@ -25,7 +25,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-enum OpKind { OP_SPACE = 0, OP_TIME = 1 };
+// OP_DECODE: time attention of a few new frames against a ring-buffer cache
+// of earlier frames' K/V (rollout); its masks are the time op's.
+enum OpKind { OP_SPACE = 0, OP_TIME = 1, OP_DECODE = 2 };
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -8,13 +8,26 @@
 namespace bca {
 
 struct AttnDims {
-  int op;                 // 0 = space, 1 = time
+  int op;                 // 0 = space, 1 = time, 2 = time over a KV cache (decode)
   int B, T, N, Hq, Hkv, D;
   int dtype;              // 0 = bf16, 1 = fp32
   int window;             // time: 0 = unbounded causal
   int agent_begin, agent_count;  // space
   float scale;            // softmax scale (> 0)
+  // decode only: the T query frames are absolute frames q_frame0 .. ; k and v
+  // hold kv_frames frames per slot, absolute frame f at position f % kv_frames
+  int kv_frames = 0;
+  int q_frame0 = 0;
 };
+
+// AttnDims::op of the decode call (the kernels' OP_DECODE).
+constexpr int OP_DECODE_ID = 2;
+
+// Key frames a decode call reads: [first, last] in absolute frame indices.
+inline void decode_key_range(const AttnDims& d, int& first, int& last) {
+  last = d.q_frame0 + d.T - 1;
+  first = (d.window > 0 && d.q_frame0 - d.window + 1 > 0) ? d.q_frame0 - d.window + 1 : 0;
+}
 
 // Largest sequence length (tokens for space, frames for time) the
 // LDS-resident MFMA backward handles; longer problems take the generic path.

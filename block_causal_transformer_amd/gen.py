@@ -28,7 +28,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from .configs import Workload
+from .configs import DecodeWorkload, Workload
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -105,3 +105,15 @@ def masked_slots(w: Workload, variant: int = 0) -> Optional[np.ndarray]:
     for _ in range(w.B * w.T):
         rows.append(begin + raux.choice(patches, size=count, replace=False))
     return np.stack(rows)
+
+
+def make_decode_inputs(w: DecodeWorkload, variant: int = 0) -> Dict[str, np.ndarray]:
+    """Draw q (B,Tq,N,Hq,D) and the ring caches k_cache, v_cache (B,C,N,Hkv,D)
+    of a decode workload: ``SeedSequence(w.seed + variant)`` spawned into q, k,
+    v streams, standard normal, rounded like ``make_inputs``.  Every ring
+    position is filled (positions the queries do not read carry values too)."""
+    ss = np.random.SeedSequence(w.seed + variant)
+    rq, rk, rv = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3)]
+    return {"q": _draw(rq, w.q_shape(), 1.0, w.dtype),
+            "k_cache": _draw(rk, w.cache_shape(), 1.0, w.dtype),
+            "v_cache": _draw(rv, w.cache_shape(), 1.0, w.dtype)}

@@ -7,9 +7,9 @@ library is not built, or a call fails, an exception is raised.
 
 Raw entry points carry the C names and arguments:
 ``space_attn_fwd``, ``space_attn_bwd``, ``time_attn_fwd``, ``time_attn_bwd``,
-``bca_bwd_workspace_bytes``, ``bca_status_string``, ``bca_last_error``,
-``bca_abi_version``.  ``attn_fwd`` / ``attn_bwd`` allocate the outputs with
-torch and call them.
+``time_attn_decode_fwd``, ``bca_bwd_workspace_bytes``, ``bca_status_string``,
+``bca_last_error``, ``bca_abi_version``.  ``attn_fwd`` / ``attn_bwd`` /
+``attn_decode_fwd`` allocate the outputs with torch and call them.
 """
 from __future__ import annotations
 
@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
 BCA_OK, BCA_ERR_INVALID_ARG, BCA_ERR_UNSUPPORTED, BCA_ERR_HIP = 0, 1, 2, 3
 BCA_BF16, BCA_F32 = 0, 1
 BCA_OP_SPACE, BCA_OP_TIME = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class BcaShape(ctypes.Structure):
@@ -49,7 +49,8 @@ _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ["space_attn_fwd", "space_attn_bwd", "time_attn_fwd", "time_attn_bwd",
-            "bca_bwd_workspace_bytes", "bca_status_string", "bca_last_error", "bca_abi_version"]
+            "time_attn_decode_fwd", "bca_bwd_workspace_bytes", "bca_status_string",
+            "bca_last_error", "bca_abi_version"]
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             f = getattr(h, name)
             f.argtypes = [SP, MP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
             f.restype = ctypes.c_int
+        h.time_attn_decode_fwd.argtypes = [SP, MP, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P]
+        h.time_attn_decode_fwd.restype = ctypes.c_int
         h.bca_bwd_workspace_bytes.argtypes = [ctypes.c_int, SP]
         h.bca_bwd_workspace_bytes.restype = ctypes.c_size_t
         h.bca_status_string.argtypes = [ctypes.c_int]
@@ -129,6 +132,13 @@ def time_attn_bwd(shape: BcaShape, mask: BcaMask, q, k, v, o, lse, dout, dq, dk,
     return load().time_attn_bwd(_ref(shape), _ref(mask), _ptr(q), _ptr(k),
                                 _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                 _ptr(dv), _ptr(workspace), workspace_bytes, stream)
+
+
+def time_attn_decode_fwd(shape: BcaShape, mask: BcaMask, q, k_cache, v_cache, cache_frames: int,
+                         q_frame0: int, o, lse, stream=None) -> int:
+    return load().time_attn_decode_fwd(_ref(shape), _ref(mask), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), cache_frames, q_frame0, _ptr(o), _ptr(lse),
+                                       stream)
 
 
 def bca_bwd_workspace_bytes(op: int, shape: BcaShape) -> int:
@@ -209,6 +219,24 @@ def attn_bwd(op: str, q, k, v, o, lse, dout, window: int = 0, agent_begin: int =
     _check(f(shape, mask, q, k, v, o, lse, dout, dq, dk, dv, workspace if need else None,
              ws_bytes if need else 0, _stream(stream)), op + "_attn_bwd")
     return dq, dk, dv
+
+
+def attn_decode_fwd(q, k_cache, v_cache, q_frame0: int, window: int = 0, scale: float = 0.0,
+                    out: Optional[Tuple] = None, stream=None):
+    """Rollout decode of time attention: q (B, Tq, N, Hq, D) are the frames
+    q_frame0 .. q_frame0 + Tq - 1; k_cache, v_cache (B, C, N, Hkv, D) hold
+    absolute frame f at position f % C.  Returns (o, lse)."""
+    import torch
+    shape = make_shape(q, k_cache)
+    mask = make_mask("time", window, 0, 0, scale)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:4], dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    _check(time_attn_decode_fwd(shape, mask, q, k_cache, v_cache, k_cache.shape[1], q_frame0,
+                                o, lse, _stream(stream)), "time_attn_decode_fwd")
+    return o, lse
 
 
 def workload_kwargs(w) -> dict:

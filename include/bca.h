@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define BCA_ABI_VERSION 1
+#define BCA_ABI_VERSION 2
 
 typedef enum {
   BCA_OK = 0,
@@ -127,6 +127,31 @@ int time_attn_bwd(const bca_shape* shape, const bca_mask* mask, const void* q,
                   const void* k, const void* v, const void* o, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* Rollout decode of time attention (forward only).  Open Dreamer articles
+ * (pro.edgex.exchange, fr-FR edition), section "Artefacts publiés": the
+ * pipeline generates rollouts and the demo streams the generated world frame
+ * by frame; section "Architecture": time layers are causal across frames.
+ * Generating new frames runs the time op restricted to their query rows, with
+ * the keys and values of earlier frames read from a cache.
+ *
+ *   shape->T       number of new (query) frames per slot, absolute frame
+ *                  indices q_frame0 .. q_frame0 + T - 1;
+ *   q, o           (B, T, N, Hq, D), lse (B, T, N, Hq) float32;
+ *   k_cache,       (B, cache_frames, N, Hkv, D): a ring holding absolute frame
+ *   v_cache        f at frame position f % cache_frames.  The caller writes the
+ *                  new frames' K and V into the ring before the call;
+ *   mask           as time_attn_fwd (causal must be 1; window 0 = unbounded).
+ * Query frame a reads frame f iff f <= a and (window == 0 or a - f <= window-1),
+ * the predicate of time_attn_fwd, so decoding frame a from a ring filled with
+ * frames up to a gives row a of time_attn_fwd over the whole sequence.  The
+ * ring must hold every frame read: (q_frame0 + T - 1) - first + 1 <=
+ * cache_frames with first = max(0, q_frame0 - window + 1) (0 if window == 0),
+ * else BCA_ERR_INVALID_ARG (also for cache_frames <= 0 or q_frame0 < 0).
+ * Ownership, alignment, errors and asynchrony as for the other calls. */
+int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q,
+                         const void* k_cache, const void* v_cache, int32_t cache_frames,
+                         int32_t q_frame0, void* o, float* lse, void* stream);
 
 /* Bytes of device workspace the backward of `op` needs for `shape`: one fp32
  * Delta = rowsum(dO * O) per (query, head), i.e. B*T*N*Hq*4 bytes.  Returns 0

@@ -143,3 +143,44 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         ops.load(str(tmp_path / "missing.so"))
+
+
+def decode_call(shape, mask, cache_frames, q_frame0, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    return ops.time_attn_decode_fwd(shape, mask, p[0], p[1], p[2], cache_frames, q_frame0, p[3], p[4])
+
+
+@pytest.mark.parametrize("T,window,cache,q0,ok", [
+    (1, 192, 191, 500, False),   # window 192 needs 192 cached frames
+    (1, 192, 192, 500, True),
+    (1, 192, 100, 99, True),     # frames 0..99 only
+    (1, 192, 99, 99, False),
+    (4, 8, 10, 30, False),       # 4 new frames with window 8 read 11 frames
+    (4, 8, 11, 30, True),
+    (2, 0, 12, 10, True),        # unbounded window: frames 0..11
+    (2, 0, 11, 10, False),
+])
+def test_decode_cache_must_hold_every_frame_read(lib, T, window, cache, q0, ok):
+    """The size check runs before any launch; valid sizes are only checked
+    for the message (not called: the pointers are fake)."""
+    shape = good_shape(T=T)
+    mask = ops.make_mask("time", window=window)
+    if ok:
+        return
+    assert decode_call(shape, mask, cache, q0) == ops.BCA_ERR_INVALID_ARG
+    assert "cannot hold" in ops.bca_last_error()
+
+
+def test_decode_rejects_bad_arguments(lib):
+    shape = good_shape(T=1)
+    mask = ops.make_mask("time", window=4)
+    assert decode_call(shape, mask, 0, 3) == ops.BCA_ERR_INVALID_ARG
+    assert decode_call(shape, mask, 4, -1) == ops.BCA_ERR_INVALID_ARG
+    assert decode_call(shape, ops.make_mask("space"), 4, 3) == ops.BCA_ERR_UNSUPPORTED
+    assert decode_call(shape, mask, 4, 3, [FAKE, 0, FAKE, FAKE, FAKE]) == ops.BCA_ERR_INVALID_ARG
+    assert "k_cache" in ops.bca_last_error()
+    assert decode_call(shape, mask, 4, 3, [FAKE, FAKE, FAKE + 8, FAKE, FAKE]) == ops.BCA_ERR_INVALID_ARG
+    assert "v_cache" in ops.bca_last_error()
+    assert decode_call(good_shape(T=1, D=48), mask, 4, 3) == ops.BCA_ERR_UNSUPPORTED
+    assert decode_call(good_shape(T=2), mask, 8, 2 ** 31 - 1) == ops.BCA_ERR_INVALID_ARG
+    assert "overflows" in ops.bca_last_error()
