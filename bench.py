@@ -20,6 +20,13 @@ stream the kernels run on.
 
     python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--no-cpu-baseline]
 
+``--workload rollout_decode`` instead times one step of frame-by-frame
+generation (section "Artefacts publiés": rollout generation, the demo
+streaming the generated world frame by frame): space attention of the new
+290-token block plus time attention of its 290 slots against a ring-buffer
+cache of the 192 frames the window reads (``--decode-batch`` environments at
+once); ``value`` is generated frames per second through that layer pair.
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -38,11 +45,14 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+TRAFFIC_FILE_DECODE = os.path.join(ROOT, "profiles", "hbm_traffic_rollout_decode.txt")
 CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
 
 
 # kernel launches of each attention call (template argument 0 = space, 1 = time)
 KERNELS = {
+    "time_decode": "attn_fwd_kernel<2>",
+    "space_fwd_block": "attn_fwd_kernel<0>",
     "space_fwd": "attn_fwd_kernel<0>",
     "time_fwd": "attn_fwd_kernel<1>",
     "space_bwd": "attn_bwd_dq_kernel<0> + attn_bwd_dkv_kernel<0>",
@@ -59,13 +69,13 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel_key: str):
+def read_traffic(kernel_key: str, path: str = TRAFFIC_FILE):
     """HBM bytes per launch of ``kernel_key`` from the committed rocprofv3
     counter summary, or None when absent or taken on other kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#") or "=" not in line:
@@ -111,6 +121,180 @@ def cpu_baseline(target_s: float = 15.0):
     }
 
 
+def roofline_of(flop, min_bytes, ms):
+    intensity = flop / min_bytes
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
+    if intensity >= ridge:
+        roof = {"bound": "mfma", "achieved": round(flop / ms / 1e9, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(min_bytes / ms / 1e6, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    return roof
+
+
+def cpu_baseline_decode(B: int, target_s: float = 12.0):
+    """The fp64 oracle on the decode step (the new block's space attention and
+    the decode time attention of its slots), repeated for ~target_s."""
+    from block_causal_transformer_amd import configs as C, gen
+    from oracle import oracle as O
+
+    wd = C.DECODE_CONFIGS["dec"].with_(B=B)
+    ws = C.get("3").with_(B=B, T=1)
+    xd, xs = gen.make_decode_inputs(wd), gen.make_inputs(ws, with_dout=False)
+
+    def run(n):
+        t0 = time.perf_counter()
+        for _ in range(n):
+            O.fwd(ws, xs["q"], xs["k"], xs["v"])
+            O.time_decode_fwd(xd["q"], xd["k_cache"], xd["v_cache"], wd.q_frame0, wd.window)
+        return time.perf_counter() - t0
+
+    dt = run(1)
+    n = max(1, min(1000, int(target_s / max(dt, 1e-3))))
+    dt = run(n)
+    return {
+        "value": n * B / dt,
+        "unit": "frames/s",
+        "cores": O.max_threads(),
+        "kind": "oracle",
+        "sample": "%d decode steps of %d environment(s): space attention of the new 290-token "
+                  "block + time attention of its slots over 192 cached frames, fp64, %.1f s"
+                  % (n, B, dt),
+    }
+
+
+def main_decode(args):
+    import torch
+    from block_causal_transformer_amd import configs as C, gen, ops
+
+    if not os.path.exists(ops.LIB_PATH):
+        from block_causal_transformer_amd import build as hip_build
+        hip_build.build()
+    ops.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B = args.decode_batch
+    wd = C.DECODE_CONFIGS["dec"].with_(B=B)
+    ws = C.get("3").with_(B=B, T=1)
+    xd, xs = gen.make_decode_inputs(wd), gen.make_inputs(ws, with_dout=False)
+    t = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
+    dq, dk, dvv = t(xd["q"]), t(xd["k_cache"]), t(xd["v_cache"])
+    sq, sk, sv = t(xs["q"]), t(xs["k"]), t(xs["v"])
+    do, dl = torch.empty_like(dq), torch.empty(dq.shape[:4], dtype=torch.float32, device=dev)
+    so, sl = torch.empty_like(sq), torch.empty(sq.shape[:4], dtype=torch.float32, device=dev)
+    dshape, dmask = ops.make_shape(dq, dk), ops.make_mask("time", window=wd.window)
+    sshape, smask = ops.make_shape(sq, sk), ops.make_mask("space", **ops.workload_kwargs(ws))
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    # A generation step is two small launches, so it is captured once in a
+    # HIP graph and replayed (the ABI calls take the capturing stream).
+    def space_op():
+        cs = torch.cuda.current_stream().cuda_stream
+        if ops.space_attn_fwd(sshape, smask, sq, sk, sv, so, sl, cs):
+            raise RuntimeError(ops.bca_last_error())
+
+    def decode_op():
+        cs = torch.cuda.current_stream().cuda_stream
+        if ops.time_attn_decode_fwd(dshape, dmask, dq, dk, dvv, wd.cache_frames, wd.q_frame0,
+                                    do, dl, cs):
+            raise RuntimeError(ops.bca_last_error())
+
+    def step():
+        space_op()
+        decode_op()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-op durations: graphs of REPS back-to-back launches of one op, so the
+    # graph launch itself is amortized (the launches rewrite the same outputs)
+    REPS = 20
+    graphs = {}
+    for key, fn, reps in (("step", step, 1), ("space_fwd_block", space_op, REPS),
+                          ("time_decode", decode_op, REPS)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        graphs[key] = g
+        for _ in range(3):
+            g.replay()
+    torch.cuda.synchronize()
+
+    def timed(g, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    op_ms = {k: timed(graphs[k], max(1, args.steps // REPS)) / REPS
+             for k in ("space_fwd_block", "time_decode")}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graphs["step"].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ops_ = {}
+    for key, fl, by in (("space_fwd_block", C.flops(ws, "fwd"), C.min_bytes(ws, "fwd")),
+                        ("time_decode", C.decode_flops(wd), C.decode_min_bytes(wd))):
+        ms = op_ms[key]
+        ops_[key] = {"ms": round(ms, 5), "tflops": round(fl / ms / 1e9, 2),
+                     "gbps": round(by / ms / 1e6, 1),
+                     "pct_hbm_peak": round(100.0 * by / ms / 1e6 / PEAK_HBM_GBPS, 2),
+                     "flop": fl, "min_bytes": by}
+    dom = max(ops_, key=lambda k: ops_[k]["ms"])
+    d = ops_[dom]
+    roof = roofline_of(d["flop"], d["min_bytes"], d["ms"])
+    roof["kernel"] = dom + " (" + KERNELS[dom] + ")"
+    # the committed counters were taken on the one-environment step
+    roof["traffic"] = read_traffic(dom, TRAFFIC_FILE_DECODE) if B == 1 else None
+    ms_step = elapsed / args.steps * 1e3
+    out = {
+        "metric": "rollout decode frames/s through one space + one time attention layer",
+        "value": round(args.steps * B / elapsed, 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "timing": "HIP graph replays: one graph per step for value; per-op figures from graphs "
+                  "of 20 back-to-back launches of the op",
+        "config": {
+            "workload": "Minecraft rollout decode step: space attention of the new 290-token "
+                        "block (30 q / 3 kv heads, d 64, agent isolation) + time attention of its "
+                        "290 slots over a ring cache of the 192 frames the window reads, %d "
+                        "environment(s)" % B,
+            "B": B, "N": wd.N, "Hq": wd.Hq, "Hkv": wd.Hkv, "D": wd.D, "window": wd.window,
+            "cache_frames": wd.cache_frames, "q_frame0": wd.q_frame0,
+        },
+        "ops": {k: {kk: vv for kk, vv in v.items() if kk not in ("flop", "min_bytes")}
+                for k, v in ops_.items()},
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_decode(B),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,11 +303,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--workload", choices=("train_step", "rollout_decode"), default="train_step")
+    ap.add_argument("--decode-batch", type=int, default=1,
+                    help="rollout_decode: environments generated at once")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the op shards by block / slot with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "rollout_decode":
+        if args.steps == 30 and args.warmup == 5:
+            args.steps, args.warmup = 200, 20
+        return main_decode(args)
 
     import torch
     from block_causal_transformer_amd import configs as C, gen, ops
@@ -221,16 +412,7 @@ def main():
     # dominant kernel: the op with the largest time share
     dom = max(per_op, key=lambda k: per_op[k]["ms"])
     d = per_op[dom]
-    dom_w = C.get("3" if dom.startswith("space") else "4")
-    intensity = d["flop"] / d["min_bytes"]
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
-    if intensity >= ridge:
-        roof = {"bound": "mfma", "achieved": round(d["flop"] / d["ms"] / 1e9, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(d["min_bytes"] / d["ms"] / 1e6, 1),
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof = roofline_of(d["flop"], d["min_bytes"], d["ms"])
     roof["kernel"] = dom + " (" + KERNELS[dom] + ")"
     roof["traffic"] = read_traffic(dom)
 

@@ -28,6 +28,7 @@ CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
 
 # attention op of each kernel (template argument 0 = space, 1 = time)
 OPS = [
+    (r"attn_fwd_kernel<2>", "time_decode"),
     (r"attn_fwd_kernel<0>", "space_fwd"),
     (r"attn_fwd_kernel<1>", "time_fwd"),
     (r"attn_bwd_dq_kernel<0>", "space_bwd"),
@@ -81,7 +82,7 @@ def cmd_stats(args):
             per_op[op] += float(r["AverageNs"]) / 1e3
     out += ["", "Average duration per attention op (sum over its kernels):", "",
             "| op | average (us) |", "|---|---|"]
-    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd"):
+    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd", "time_decode"):
         if op in per_op:
             out.append("| %s | %.1f |" % (op, per_op[op]))
     out.append("")
@@ -137,7 +138,7 @@ def cmd_traffic(args):
             avg = sum(vs) / len(vs)
             out.append("%s.%s.kib_per_dispatch=%.1f  # %s" % (op, cname.lower(), avg, kname))
             ops[op] += avg * 1024.0 * fac
-    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd"):
+    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd", "time_decode"):
         if op in ops:
             out.append("%s.bytes=%.0f" % (op, ops[op]))
     out.append("")

@@ -84,3 +84,30 @@ def test_decode_equals_full_sequence_rows():
         got = {"o": U.to_np(o)[:, 0], "lse": U.to_np(lse)[:, 0]}
         want = {"o": U.to_np(o_full)[:, t], "lse": U.to_np(lse_full)[:, t]}
         print(t, U.assert_close(w, got, want, "frame %d" % t))
+
+
+def test_decode_graph_replays_match_eager():
+    """A decode call captured in a HIP graph gives the eager result on every
+    replay, with eager work and synchronizations between the replays."""
+    _needs_gpu()
+    import torch
+    w = CASES["four_new_frames"]
+    x = gen.make_decode_inputs(w)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
+    q, kc, vc = dev(x["q"]), dev(x["k_cache"]), dev(x["v_cache"])
+    o_ref, l_ref = ops.attn_decode_fwd(q, kc, vc, w.q_frame0, window=w.window)
+    o = torch.zeros_like(o_ref)
+    lse = torch.zeros_like(l_ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.attn_decode_fwd(q, kc, vc, w.q_frame0, window=w.window, out=(o, lse))
+    for r in range(4):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), "replay %d o" % r
+        assert torch.equal(lse.view(torch.int32), l_ref.view(torch.int32)), "replay %d lse" % r
+        ops.attn_decode_fwd(q, kc, vc, w.q_frame0, window=w.window)  # eager work between
