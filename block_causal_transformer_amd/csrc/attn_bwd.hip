@@ -1,6 +1,8 @@
-// Backward of space and time attention, bf16 in/out, head_dim 64, for
-// problems of at most 320 positions (the dynamics model's 290-token blocks
-// and 256-frame slots), on gfx950.
+// Backward of space and time attention, bf16 in/out, head_dim 64, on gfx950.
+// Problems of up to 320 positions (the dynamics model's 290-token blocks and
+// 256-frame slots) keep all their keys in one LDS block; longer ones (the
+// tokenizer's 1432-token frames, long time windows) are cut into key blocks
+// of at most 320.
 //
 // Open Dreamer articles (pro.edgex.exchange, fr-FR edition), sections
 // "Architecture" and "Configuration d'entraînement" (masks, GQA), and section
@@ -44,7 +46,7 @@ namespace bca {
 
 namespace {
 
-constexpr int KMAX = kMfmaBwdMaxLen;  // 320
+constexpr int KMAX = kBwdKeyBlock;  // 320
 
 struct BwdParams {
   const bf16* q;
@@ -61,6 +63,7 @@ struct BwdParams {
   int window, agent_begin, agent_count;
   float scale, scale_log2, inv_g;
   int splits, rows_per_split;  // dq kernel
+  int kvb, kbl;                // dkv kernel: key blocks per problem, keys per block
 };
 
 // ------------------------------------------------------------- dq kernel
@@ -108,28 +111,42 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
-  const int lp32 = (p.L + 31) & ~31;
-
-  for (int idx = tid; idx < lp32 * 8; idx += NT) {
-    const int r = idx >> 3, c = idx & 7;
-    const bool ok = r < p.L;
-    const bf16x8 kv = ok ? ld_global16(kbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
-    const bf16x8 vv = ok ? ld_global16(vbase + (int64_t)r * gk.pos_stride + c * 8) : zero8();
-    st_lds16(sm.K + krow_off(r, c), kv);
-    st_lds16(sm.V + krow_off(r, c), vv);
-    const int pp = kperm(r);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sm.KT[kt_off(c * 8 + e, pp)] = kv[e];
-  }
-  __syncthreads();
-
   const int row0 = split * p.rows_per_split;
   const int row1 = min(p.rows, row0 + p.rows_per_split);
   const int nch = (row1 - row0 + DQ_QC - 1) / DQ_QC;
 
+  // Keys [wklo, wkhi) are all that any row of this workgroup sees; they pass
+  // through LDS in blocks of up to KMAX keys (one block, staged once, for the
+  // dynamics shapes), at LDS position key - key0 (rows past the block's end
+  // zero-filled up to a multiple of 32).  Keys staged as padding are never
+  // counted twice: a step that reaches past the block end is masked, because
+  // those keys lie beyond every row's range or past L.
+  int wklo, wkhi;
+  key_range(md, row0 / G, (row1 - 1) / G, wklo, wkhi);
+  wklo &= ~31;  // steps stay aligned to 32 keys (the extra keys are masked)
+  const int nkb = (wkhi - wklo + KMAX - 1) / KMAX;
+  auto stage = [&](int key0, int kn) {
+    const int lp32 = (kn + 31) & ~31;
+    for (int idx = tid; idx < lp32 * 8; idx += NT) {
+      const int r = idx >> 3, c = idx & 7;
+      const bool ok = r < kn;
+      const int64_t off = (int64_t)(key0 + (ok ? r : 0)) * gk.pos_stride + c * 8;
+      const bf16x8 kv = ok ? ld_global16(kbase + off) : zero8();
+      const bf16x8 vv = ok ? ld_global16(vbase + off) : zero8();
+      st_lds16(sm.K + krow_off(r, c), kv);
+      st_lds16(sm.V + krow_off(r, c), vv);
+      const int pp = kperm(r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.KT[kt_off(c * 8 + e, pp)] = kv[e];
+    }
+  };
+  if (nkb == 1) {
+    stage(wklo, wkhi - wklo);
+    __syncthreads();
+  }
+
   // Per chunk, this lane's query column in each of the two 16-column tiles
-  // (padding columns read a real, clamped row and are never stored).  The
-  // next chunk's Q, dO, O and LSE are loaded while the current one computes.
+  // (padding columns read a real, clamped row and are never stored).
   struct ChunkIn {
     bf16x8 q[2][2], d[2][2], o[2][2];
     float lse[2];
@@ -151,99 +168,121 @@ void attn_bwd_dq_kernel(BwdParams p) {
       in.lse[qt] = p.lse[gl.base + (int64_t)pos * gl.pos_stride + g * G + hq];
     }
   };
-  for (int ch = wave; ch < nch; ch += DQ_W) {
+  // one chunk per wave and pass; with several key blocks, every block is
+  // staged once per pass and each wave accumulates its chunk's dQ over them
+  const int passes = (nch + DQ_W - 1) / DQ_W;
+  for (int pass = 0; pass < passes; ++pass) {
+    const int ch = pass * DQ_W + wave;
+    const bool active = ch < nch;
     const int r0 = row0 + ch * DQ_QC;
-    ChunkIn nxt;
-    load_chunk(ch, nxt);
     bf16x8 qreg[2][2], dreg[2][2];
     int qpos[2], hh[2];
     bool qv[2];
     float lse2[2], dlt[2];
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const int r = r0 + qt * 16 + li;
-      qv[qt] = r < row1;
-      const int rr = min(r, row1 - 1);
-      qpos[qt] = row_pos(rr, p.inv_g);
-      hh[qt] = rr - qpos[qt] * G;
-      float part = 0.f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        qreg[qt][s] = nxt.q[qt][s];
-        dreg[qt][s] = nxt.d[qt][s];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)nxt.d[qt][s][e], (float)nxt.o[qt][s][e], part);
-      }
-      dlt[qt] = group4_sum(part);
-      lse2[qt] = qv[qt] ? nxt.lse[qt] * kLog2e : INFINITY;
-    }
     f32x4 acc[4][2];
+    int qlo = 0, qhi = 0, klo = 0, khi = 0;
+    if (active) {
+      ChunkIn nxt;
+      load_chunk(ch, nxt);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      acc[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    const int qlo = r0 / G;
-    const int qhi = (min(r0 + DQ_QC, row1) - 1) / G;
-    int klo, khi;
-    key_range(md, qlo, qhi, klo, khi);
-    const int st0 = klo >> 5, st1 = (khi + 31) >> 5;
-    for (int st = st0; st < st1; ++st) {
-      const int kabs = st * 32;
-      f32x4 sc[2][2], dp[2][2];
+      for (int qt = 0; qt < 2; ++qt) {
+        const int r = r0 + qt * 16 + li;
+        qv[qt] = r < row1;
+        const int rr = min(r, row1 - 1);
+        qpos[qt] = row_pos(rr, p.inv_g);
+        hh[qt] = rr - qpos[qt] * G;
+        float part = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kr = kabs + h * 16 + li;
-        const bf16x8 k0 = ld_lds16(sm.K + krow_off(kr, lg));
-        const bf16x8 k1 = ld_lds16(sm.K + krow_off(kr, 4 + lg));
-        const bf16x8 v0 = ld_lds16(sm.V + krow_off(kr, lg));
-        const bf16x8 v1 = ld_lds16(sm.V + krow_off(kr, 4 + lg));
+        for (int s = 0; s < 2; ++s) {
+          qreg[qt][s] = nxt.q[qt][s];
+          dreg[qt][s] = nxt.d[qt][s];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          z = mfma16(k0, qreg[qt][0], z);
-          sc[qt][h] = mfma16(k1, qreg[qt][1], z);
-          // the accumulator starts at -Delta, so it ends at dP - Delta
-          f32x4 y = {-dlt[qt], -dlt[qt], -dlt[qt], -dlt[qt]};
-          y = mfma16(v0, dreg[qt][0], y);
-          dp[qt][h] = mfma16(v1, dreg[qt][1], y);
+          for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)nxt.d[qt][s][e], (float)nxt.o[qt][s][e], part);
         }
-      }
-      bf16x8 dsb[2];
-      if (tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x4 d0, d1;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            d0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt])) * dp[qt][0][j];
-            d1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt])) * dp[qt][1][j];
-          }
-          dsb[qt] = pack8(d0, d1);
-        }
-      } else {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          f32x4 d0, d1;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bool vis0 = visible_op<OP>(md, qpos[qt], kabs + lg * 4 + j);
-            const bool vis1 = visible_op<OP>(md, qpos[qt], kabs + 16 + lg * 4 + j);
-            const float e0 = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt])) * dp[qt][0][j];
-            const float e1 = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt])) * dp[qt][1][j];
-            d0[j] = vis0 ? e0 : 0.f;
-            d1[j] = vis1 ? e1 : 0.f;
-          }
-          dsb[qt] = pack8(d0, d1);
-        }
+        dlt[qt] = group4_sum(part);
+        lse2[qt] = qv[qt] ? nxt.lse[qt] * kLog2e : INFINITY;
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const bf16x8 kt = ld_lds16(sm.KT + kt_off(dt * 16 + li, kabs + lg * 8));
-        acc[dt][0] = mfma16(kt, dsb[0], acc[dt][0]);
-        acc[dt][1] = mfma16(kt, dsb[1], acc[dt][1]);
+        acc[dt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[dt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      qlo = r0 / G;
+      qhi = (min(r0 + DQ_QC, row1) - 1) / G;
+      key_range(md, qlo, qhi, klo, khi);
+    }
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int key0 = wklo + kb * KMAX;
+      const int kn = min(KMAX, wkhi - key0);
+      if (nkb > 1) {
+        __syncthreads();
+        stage(key0, kn);
+        __syncthreads();
+      }
+      if (!active) continue;
+      const int lo = max(klo, key0), hi = min(khi, key0 + kn);
+      if (lo >= hi) continue;
+      const int st0 = (lo - key0) >> 5, st1 = (hi - key0 + 31) >> 5;
+      for (int st = st0; st < st1; ++st) {
+        const int kabs = key0 + st * 32;  // absolute key of the step's first row
+        f32x4 sc[2][2], dp[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kr = st * 32 + h * 16 + li;
+          const bf16x8 k0 = ld_lds16(sm.K + krow_off(kr, lg));
+          const bf16x8 k1 = ld_lds16(sm.K + krow_off(kr, 4 + lg));
+          const bf16x8 v0 = ld_lds16(sm.V + krow_off(kr, lg));
+          const bf16x8 v1 = ld_lds16(sm.V + krow_off(kr, 4 + lg));
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = mfma16(k0, qreg[qt][0], z);
+            sc[qt][h] = mfma16(k1, qreg[qt][1], z);
+            // the accumulator starts at -Delta, so it ends at dP - Delta
+            f32x4 y = {-dlt[qt], -dlt[qt], -dlt[qt], -dlt[qt]};
+            y = mfma16(v0, dreg[qt][0], y);
+            dp[qt][h] = mfma16(v1, dreg[qt][1], y);
+          }
+        }
+        bf16x8 dsb[2];
+        if (tile_all_visible(md, qlo, qhi, kabs, kabs + 32) && kabs + 32 <= key0 + kn) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            f32x4 d0, d1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              d0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt])) * dp[qt][0][j];
+              d1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt])) * dp[qt][1][j];
+            }
+            dsb[qt] = pack8(d0, d1);
+          }
+        } else {
+          const int kend = key0 + kn;
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) {
+            f32x4 d0, d1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int ka = kabs + lg * 4 + j, kc = kabs + 16 + lg * 4 + j;
+              const bool vis0 = visible_op<OP>(md, qpos[qt], ka) & (ka < kend);
+              const bool vis1 = visible_op<OP>(md, qpos[qt], kc) & (kc < kend);
+              const float e0 = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -lse2[qt])) * dp[qt][0][j];
+              const float e1 = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -lse2[qt])) * dp[qt][1][j];
+              d0[j] = vis0 ? e0 : 0.f;
+              d1[j] = vis1 ? e1 : 0.f;
+            }
+            dsb[qt] = pack8(d0, d1);
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8 kt = ld_lds16(sm.KT + kt_off(dt * 16 + li, st * 32 + lg * 8));
+          acc[dt][0] = mfma16(kt, dsb[0], acc[dt][0]);
+          acc[dt][1] = mfma16(kt, dsb[1], acc[dt][1]);
+        }
       }
     }
+    if (!active) continue;
     // Delta is stored only now so that no wait on the store delays the
     // first products of the chunk
 #pragma unroll
@@ -300,8 +339,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amd
 void attn_bwd_dkv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) KvBuf sbuf[2];
 
-  int ug, wg;
-  xcd_remap(blockIdx.x, p.units * p.Hkv, 1, ug, wg);
+  // workgroup = (problem, block of kbl keys); one block for L <= 320
+  int ug, kb;
+  xcd_remap(blockIdx.x, p.units * p.Hkv, p.kvb, ug, kb);
   const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
   const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, 64);
   const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
@@ -313,7 +353,9 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
-  const int nkt = (p.L + 15) >> 4;
+  const int kb0 = kb * p.kbl;                 // first key of the block
+  const int kend = min(p.L, kb0 + p.kbl);      // one past its last key
+  const int nkt = (kend - kb0 + 15) >> 4;
 
   // K and V operands of the wave's tiles, straight from global memory
   // (keys past the end read as zero)
@@ -323,8 +365,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   bool keyok[KV_TPW];
 #pragma unroll
   for (int m = 0; m < KV_TPW; ++m) {
-    const int key = (wave + KV_W * m) * 16 + li;
-    const bool ok = key < p.L;
+    const int key = kb0 + (wave + KV_W * m) * 16 + li;
+    const bool ok = key < kend;
     const int64_t off = gk.base + (int64_t)min(key, p.L - 1) * gk.pos_stride + g * 64;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -381,13 +423,23 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     }
   };
 
-  const int nchunks = (p.rows + KV_QC - 1) / KV_QC;
-  fetch(0);
-  stage(sbuf[0]);
-  if (1 < nchunks) fetch(1);
+  // query chunks that can see a key of the block: time attention skips the
+  // rows before it and those more than the window after it
+  int c_lo = 0, c_hi = (p.rows + KV_QC - 1) / KV_QC;
+  if (OP == OP_TIME) {
+    c_lo = (kb0 * G) / KV_QC;
+    if (p.window > 0) {
+      const int64_t rend = min((int64_t)p.rows, (int64_t)(kend - 1 + p.window) * G);
+      c_hi = min(c_hi, (int)((rend + KV_QC - 1) / KV_QC));
+    }
+  }
+  const int nchunks = c_hi;
+  fetch(c_lo);
+  stage(sbuf[c_lo & 1]);
+  if (c_lo + 1 < nchunks) fetch(c_lo + 1);
   __syncthreads();
 
-  for (int c = 0; c < nchunks; ++c) {
+  for (int c = c_lo; c < nchunks; ++c) {
     KvBuf& b = sbuf[c & 1];
     const int r0 = c * KV_QC;
     const int qlo = r0 / G;
@@ -398,7 +450,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
     for (int m = 0; m < KV_TPW; ++m) {
       const int t = wave + KV_W * m;
-      const int k0 = t * 16, k1 = min(t * 16 + 16, p.L);
+      const int k0 = kb0 + t * 16, k1 = min(k0 + 16, kend);
       work[m] = t < nkt && !tile_none_visible(md, qlo, qhi, k0, k1);
       if (OP == OP_TIME)
         edge[m] = !tile_all_visible(md, qlo, qhi, k0, k1);
@@ -490,8 +542,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
 
 #pragma unroll
   for (int m = 0; m < KV_TPW; ++m) {
-    const int key = (wave + KV_W * m) * 16 + li;
-    if (key >= p.L) continue;
+    const int key = kb0 + (wave + KV_W * m) * 16 + li;
+    if (key >= kend) continue;
     bf16* dkd = p.dk + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
     bf16* dvd = p.dv + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
 #pragma unroll
@@ -536,7 +588,7 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.scale = d.scale;
   p.scale_log2 = d.scale * kLog2e;
   p.inv_g = 1.0f / (float)p.G;
-  if (p.L > KMAX || p.G > 256) return hipErrorInvalidValue;
+  if (p.G > 256 || (long)p.rows >= (1L << 21)) return hipErrorInvalidValue;
   const long problems = (long)p.units * p.Hkv;
 
   // dq kernel: one workgroup per CU (LDS), rows split so the grid covers the
@@ -549,8 +601,11 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.rows_per_split = per * DQ_QC;
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
   const long g1 = problems * p.splits;
-  // dkv kernel: one workgroup per problem (20 tile slots cover 320 keys)
-  const long g2 = problems;
+  // dkv kernel: one workgroup per problem and block of at most 320 keys (the
+  // 24 tile slots of its 8 waves), blocks of equal size in whole tiles
+  p.kvb = (p.L + KMAX - 1) / KMAX;
+  p.kbl = (((p.L + p.kvb - 1) / p.kvb) + 15) & ~15;
+  const long g2 = problems * p.kvb;
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 
   if (d.op == OP_SPACE) {

@@ -29,9 +29,10 @@ inline void decode_key_range(const AttnDims& d, int& first, int& last) {
   first = (d.window > 0 && d.q_frame0 - d.window + 1 > 0) ? d.q_frame0 - d.window + 1 : 0;
 }
 
-// Largest sequence length (tokens for space, frames for time) the
-// LDS-resident MFMA backward handles; longer problems take the generic path.
-constexpr int kMfmaBwdMaxLen = 320;
+// Keys per LDS block of the MFMA backward: the dq kernel streams longer
+// problems through LDS in blocks of this many keys, and the dkv kernel gives
+// every such block its own workgroup.
+constexpr int kBwdKeyBlock = 320;
 
 // MFMA kernels: bf16, D = 64.
 hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k, const void* v,
@@ -51,11 +52,9 @@ hipError_t launch_attn_bwd_generic(const AttnDims& d, const void* q, const void*
                                    const void* dout, void* dq, void* dk, void* dv,
                                    float* delta_ws, hipStream_t stream);
 
-// True when the backward of these dims runs on the MFMA kernel.
-inline bool bwd_uses_mfma(const AttnDims& d) {
-  const int L = d.op == 0 ? d.N : d.T;
-  return d.dtype == 0 && d.D == 64 && L <= kMfmaBwdMaxLen;
-}
+// True when the backward of these dims runs on the MFMA kernels (bf16,
+// head_dim 64, any length).
+inline bool bwd_uses_mfma(const AttnDims& d) { return d.dtype == 0 && d.D == 64; }
 
 inline bool fwd_uses_mfma(const AttnDims& d) { return d.dtype == 0 && d.D == 64; }
 

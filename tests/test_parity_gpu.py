@@ -89,6 +89,13 @@ RAGGED += [
     C.Workload("time_d32_bf16", "time", 1, 9, 3, 4, 2, 32, "bf16", 3, 0, 0, 1.0, 9006),
     C.Workload("space_d64_f32", "space", 1, 2, 21, 4, 2, 64, "f32", 0, 20, 1, 1.0, 9007),
     C.Workload("time_d64_f32", "time", 1, 12, 2, 4, 1, 64, "f32", 5, 0, 0, 1.0, 9008),
+    # longer than one 320-key block: key blocks in the dq and dkv kernels
+    C.Workload("space_N641", "space", 1, 1, 641, 6, 2, 64, "bf16", 0, 640, 1, 1.0, 9010),
+    C.Workload("space_N1432_dense", "space", 1, 1, 1432, 4, 4, 64, "bf16", 0, 0, 0, 1.0, 9011),
+    C.Workload("space_N700_agent_mid", "space", 1, 1, 700, 4, 2, 64, "bf16", 0, 333, 2, 1.0, 9012),
+    C.Workload("time_T1024_W192", "time", 1, 1024, 2, 6, 2, 64, "bf16", 192, 0, 0, 1.0, 9013),
+    C.Workload("time_T700_W0", "time", 1, 700, 1, 6, 2, 64, "bf16", 0, 0, 0, 1.0, 9014),
+    C.Workload("time_T650_W333", "time", 1, 650, 2, 3, 1, 64, "bf16", 333, 0, 0, 1.0, 9015),
 ]
 
 
