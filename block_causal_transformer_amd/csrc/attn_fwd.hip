@@ -101,10 +101,15 @@ void attn_fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
-  const int nkb = (p.L + KMAX - 1) / KMAX;
   const int nch = (row1 - row0 + QCH - 1) / QCH;
   const int passes = (nch + FW - 1) / FW;
   const int G = p.G;
+  // keys [wklo, wkhi) are all that any row of this workgroup sees (32-key
+  // aligned start); they pass through LDS in blocks of up to KMAX keys
+  int wklo, wkhi;
+  key_range(md, row0 / G + qsh, (row1 - 1) / G + qsh, wklo, wkhi);
+  wklo &= ~31;
+  const int nkb = (wkhi - wklo + KMAX - 1) / KMAX;
 
   // this lane's query column in each 16-column tile of a chunk; padding
   // columns read a real (clamped) row and are never stored.  The next
@@ -151,8 +156,8 @@ void attn_fwd_kernel(FwdParams p) {
     }
 
     for (int kb = 0; kb < nkb; ++kb) {
-      const int key0 = kb * KMAX;
-      const int kn = min(KMAX, p.L - key0);
+      const int key0 = wklo + kb * KMAX;
+      const int kn = min(KMAX, wkhi - key0);
       if (nkb > 1 || pass == 0) {
         if (nkb > 1) __syncthreads();
         const int lp = (kn + 31) & ~31;
