@@ -303,7 +303,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
-    ap.add_argument("--workload", choices=("train_step", "rollout_decode"), default="train_step")
+    ap.add_argument("--workload", choices=("train_step", "tokenizer_step", "long_time", "rollout_decode"),
+                    default="train_step")
     ap.add_argument("--decode-batch", type=int, default=1,
                     help="rollout_decode: environments generated at once")
     args = ap.parse_args()
@@ -316,6 +317,33 @@ def main():
             args.steps, args.warmup = 200, 20
         return main_decode(args)
 
+    return main_step(args)
+
+
+def step_workloads(name):
+    """(workloads, description, metric) of a fwd+bwd step workload."""
+    from block_causal_transformer_amd import configs as C
+    if name == "train_step":
+        return ([C.get("3"), C.get("4")],
+                "Minecraft dynamics attention step: space layer fwd+bwd (B=4 x T=64 blocks of 290 "
+                "tokens, 30 q / 3 kv heads, d 64, agent isolation) + time layer fwd+bwd (T=256 "
+                "frames x 290 slots, causal, window 192)",
+                "block-causal attention TFLOP/s (fwd, fwd+bwd) and % of MI355X bf16 MFMA peak")
+    if name == "tokenizer_step":
+        return ([C.get("5a"), C.get("5b"), C.get("5c")],
+                "Tokenizer attention step: encoder space layer (16 frames of 1432 tokens, 24 heads "
+                "MHA, dense) + decoder space layer (16 heads) + decoder time layer (1432 slots x 16 "
+                "frames, causal, window 16), each fwd+bwd",
+                "tokenizer attention TFLOP/s (fwd+bwd) and % of MI355X bf16 MFMA peak")
+    if name == "long_time":
+        return ([C.get("4").with_(name="4L", T=1024, seed=4100)],
+                "Long-sequence time layer fwd+bwd: T=1024 frames x 290 slots, 30 q / 3 kv heads, "
+                "d 64, causal, window 192",
+                "long-sequence time attention TFLOP/s (fwd+bwd) and % of MI355X bf16 MFMA peak")
+    raise ValueError(name)
+
+
+def main_step(args):
     import torch
     from block_causal_transformer_amd import configs as C, gen, ops
 
@@ -326,9 +354,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    ws, wt = C.get("3"), C.get("4")
+    wls, desc, metric = step_workloads(args.workload)
     bufs = {}
-    for w in (ws, wt):
+    for w in wls:
         x = gen.make_inputs(w)
         b = {k: torch.from_numpy(v).to(dev).to(torch.bfloat16) for k, v in x.items()}
         del x
@@ -343,13 +371,14 @@ def main():
                                            b["shape"])
         b["ws"] = torch.empty(max(need, 16), dtype=torch.uint8, device=dev) if need else None
         b["ws_bytes"] = need
+        b["w"] = w
         bufs[w.name] = b
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
     def call(name, direction):
         b = bufs[name]
-        w = C.get(name)
+        w = b["w"]
         if direction == "fwd":
             f = ops.space_attn_fwd if w.op == "space" else ops.time_attn_fwd
             rc = f(b["shape"], b["mask"], b["q"], b["k"], b["v"], b["o"], b["lse"], sp)
@@ -360,9 +389,12 @@ def main():
         if rc != 0:
             raise RuntimeError("%s %s: %s" % (name, direction, ops.bca_last_error()))
 
-    seq = [("3", "fwd"), ("3", "bwd"), ("4", "fwd"), ("4", "bwd")]
-    labels = {("3", "fwd"): "space_fwd", ("3", "bwd"): "space_bwd",
-              ("4", "fwd"): "time_fwd", ("4", "bwd"): "time_bwd"}
+    seq = [(w.name, d) for w in wls for d in ("fwd", "bwd")]
+    if args.workload == "train_step":
+        labels = {("3", "fwd"): "space_fwd", ("3", "bwd"): "space_bwd",
+                  ("4", "fwd"): "time_fwd", ("4", "bwd"): "time_bwd"}
+    else:
+        labels = {(n, d): "%s_%s_%s" % (n, bufs[n]["w"].op, d) for n, d in seq}
 
     for _ in range(args.warmup):
         for name, d in seq:
@@ -372,11 +404,11 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        evs[s][0].record(stream)
+    for s_ in range(args.steps):
+        evs[s_][0].record(stream)
         for i, (name, d) in enumerate(seq):
             call(name, d)
-            evs[s][i + 1].record(stream)
+            evs[s_][i + 1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
@@ -392,8 +424,8 @@ def main():
     per_op = {}
     total_flops = 0.0
     for i, key in enumerate(seq):
-        w = C.get(key[0])
-        ms = sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
+        w = bufs[key[0]]["w"]
+        ms = sum(evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)) / args.steps
         fl = C.flops(w, key[1])
         by = C.min_bytes(w, key[1])
         total_flops += fl
@@ -405,6 +437,7 @@ def main():
             "pct_hbm_peak": round(100.0 * by / ms / 1e6 / PEAK_HBM_GBPS, 2),
             "flop": fl,
             "min_bytes": by,
+            "op": "%s_%s" % (w.op, key[1]),
         }
     ms_step = elapsed / args.steps * 1e3
     value = total_flops * args.steps / elapsed / 1e12
@@ -413,11 +446,23 @@ def main():
     dom = max(per_op, key=lambda k: per_op[k]["ms"])
     d = per_op[dom]
     roof = roofline_of(d["flop"], d["min_bytes"], d["ms"])
-    roof["kernel"] = dom + " (" + KERNELS[dom] + ")"
-    roof["traffic"] = read_traffic(dom)
+    roof["kernel"] = dom + " (" + KERNELS[d["op"]] + ")"
+    roof["traffic"] = read_traffic(dom) if args.workload == "train_step" else None
 
+    cfg = {"workload": desc}
+    for w in wls:
+        cfg[w.name] = {"op": w.op, "B": w.B, "T": w.T, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv,
+                       "D": w.D, "window": w.window, "agent_begin": w.agent_begin,
+                       "agent_count": w.agent_count}
+    cfg["flop_per_step"] = total_flops
+    if args.workload == "train_step":
+        cfg = {"workload": desc,
+               "space": {k: v for k, v in cfg["3"].items() if k not in ("op", "window")},
+               "time": {k: v for k, v in cfg["4"].items()
+                        if k not in ("op", "agent_begin", "agent_count")},
+               "flop_per_step": total_flops}
     out = {
-        "metric": "block-causal attention TFLOP/s (fwd, fwd+bwd) and % of MI355X bf16 MFMA peak",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -429,28 +474,53 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": "Minecraft dynamics attention step: space layer fwd+bwd (B=4 x T=64 blocks "
-                        "of 290 tokens, 30 q / 3 kv heads, d 64, agent isolation) + time layer "
-                        "fwd+bwd (T=256 frames x 290 slots, causal, window 192)",
-            "space": {"B": ws.B, "T": ws.T, "N": ws.N, "Hq": ws.Hq, "Hkv": ws.Hkv, "D": ws.D,
-                      "agent_begin": ws.agent_begin, "agent_count": ws.agent_count},
-            "time": {"B": wt.B, "T": wt.T, "N": wt.N, "Hq": wt.Hq, "Hkv": wt.Hkv, "D": wt.D,
-                     "window": wt.window},
-            "flop_per_step": total_flops,
-        },
+        "config": cfg,
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "fwd_tflops": round((per_op["space_fwd"]["flop"] + per_op["time_fwd"]["flop"])
-                            / (per_op["space_fwd"]["ms"] + per_op["time_fwd"]["ms"]) / 1e9, 2),
-        "ops": {k: {kk: vv for kk, vv in v.items() if kk not in ("flop", "min_bytes")}
+        "ops": {k: {kk: vv for kk, vv in v.items() if kk not in ("flop", "min_bytes", "op")}
                 for k, v in per_op.items()},
         "roofline": roof,
     }
+    if args.workload == "train_step":
+        out["fwd_tflops"] = round((per_op["space_fwd"]["flop"] + per_op["time_fwd"]["flop"])
+                                  / (per_op["space_fwd"]["ms"] + per_op["time_fwd"]["ms"]) / 1e9, 2)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline() if args.workload == "train_step" else cpu_baseline_ops(wls)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_ops(wls, target_s: float = 15.0):
+    """The fp64 oracle on a bounded sample of each workload of the step (a few
+    whole units of each, fwd + bwd), scaled to the same TFLOP/s unit."""
+    from block_causal_transformer_amd import configs as C, gen
+    from oracle import oracle as O
+
+    def sample(w, n):
+        return w.with_(B=1, T=n) if w.op == "space" else w.with_(B=1, N=n)
+
+    def run(n):
+        t0 = time.perf_counter()
+        fl = 0.0
+        for w in wls:
+            ws_ = sample(w, n)
+            x = gen.make_inputs(ws_)
+            O.fwd(ws_, x["q"], x["k"], x["v"])
+            O.bwd(ws_, x["q"], x["k"], x["v"], x["dout"])
+            fl += C.flops(ws_, "fwd") + C.flops(ws_, "bwd")
+        return time.perf_counter() - t0, fl
+
+    dt, _ = run(1)
+    n = max(1, min(64, int(target_s / max(dt, 1e-3))))
+    dt, fl = run(n)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.max_threads(),
+        "kind": "oracle",
+        "sample": "%d unit(s) (blocks / slots) of each of %s, forward + backward, fp64, %.1f s"
+                  % (n, ", ".join(w.name for w in wls), dt),
+    }
 
 
 if __name__ == "__main__":
