@@ -332,6 +332,66 @@ int oracle_time_decode_fwd(int B, int Tq, int N, int Hq, int Hkv, int D, int win
   return 0;
 }
 
+/* ---- projections beside attention ----
+ * Open Dreamer articles (pro.edgex.exchange, fr-FR edition), section
+ * "Configuration d'entraînement": d_model 1920, 30 query heads over 3 KV
+ * heads of width 64; section "Ingénierie de la stabilité", item 3: parameters
+ * are kept in fp32, bf16 covers most matmul activations and the attention
+ * inputs, normalization layers stay in fp32.  Readings (the pages name no
+ * norm and no layout): the norm before the QKV projection is an RMS norm with
+ * a learned fp32 gain; its output is the bf16 matmul activation; weights are
+ * bf16 copies stored (out_features, in_features); QKV output columns are the
+ * Q heads, then the K heads, then the V heads; no biases.
+ *
+ * bf16(x): x rounded to the nearest value with 8 significant bits, ties to
+ * even (finite, normal range). */
+static double round_bf16(double x) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  const double m = frexp(x, &e);           /* x = m * 2^e, 0.5 <= |m| < 1 */
+  return ldexp(nearbyint(m * 256.0), e - 8); /* default rounding: to nearest even */
+}
+
+/* RMS norm then the QKV projection.  x (M, dm); gamma (dm); w ((Hq+2Hkv)*D, dm);
+ * q (M, Hq*D), k and v (M, Hkv*D); rstd (M) = 1/sqrt(mean(x^2) + eps).
+ *   y = bf16(x * rstd * gamma),  [q | k | v] = y w^T. */
+int oracle_rmsnorm_qkv_fwd(long M, int dm, int Hq, int Hkv, int D, double eps,
+                           const double* x, const double* gamma, const double* w,
+                           double* q, double* k, double* v, double* rstd) {
+  if (M <= 0 || dm <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || eps < 0.0) return -1;
+  const int nq = Hq * D, nkv = Hkv * D, nout = nq + 2 * nkv;
+#pragma omp parallel for schedule(static)
+  for (long m = 0; m < M; ++m) {
+    const double* xm = x + m * dm;
+    double ss = 0.0;
+    for (int c = 0; c < dm; ++c) ss += xm[c] * xm[c];
+    const double r = 1.0 / sqrt(ss / dm + eps);
+    rstd[m] = r;
+    double* y = (double*)malloc(sizeof(double) * dm);
+    for (int c = 0; c < dm; ++c) y[c] = round_bf16(xm[c] * r * gamma[c]);
+    for (int n = 0; n < nout; ++n) {
+      const double acc = dot(y, w + (long)n * dm, dm);
+      if (n < nq) q[m * nq + n] = acc;
+      else if (n < nq + nkv) k[m * nkv + (n - nq)] = acc;
+      else v[m * nkv + (n - nq - nkv)] = acc;
+    }
+    free(y);
+  }
+  return 0;
+}
+
+/* Output projection with the residual add: o (M, din); w (dm, din);
+ * residual (M, dm) or NULL;  y = residual + o w^T, (M, dm). */
+int oracle_out_proj_fwd(long M, int dm, int din, const double* o, const double* w,
+                        const double* residual, double* y) {
+  if (M <= 0 || dm <= 0 || din <= 0) return -1;
+#pragma omp parallel for schedule(static)
+  for (long m = 0; m < M; ++m)
+    for (int n = 0; n < dm; ++n)
+      y[m * dm + n] = (residual ? residual[m * dm + n] : 0.0) + dot(o + m * din, w + (long)n * din, din);
+  return 0;
+}
+
 void oracle_set_threads(int n) {
 #ifdef _OPENMP
   if (n > 0) omp_set_num_threads(n);

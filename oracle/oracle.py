@@ -46,6 +46,11 @@ def _declare(h: ctypes.CDLL) -> ctypes.CDLL:
     h.oracle_time_fwd.argtypes = [i] * 6 + [i, d] + [_DP] * 5
     h.oracle_time_bwd.argtypes = [i] * 6 + [i, d] + [_DP] * 7
     h.oracle_time_decode_fwd.argtypes = [i] * 7 + [d, i, i] + [_DP] * 5
+    L = ctypes.c_long
+    h.oracle_rmsnorm_qkv_fwd.argtypes = [L, i, i, i, i, d] + [_DP] * 7
+    h.oracle_rmsnorm_qkv_fwd.restype = ctypes.c_int
+    h.oracle_out_proj_fwd.argtypes = [L, i, i, _DP, _DP, _DP, _DP]
+    h.oracle_out_proj_fwd.restype = ctypes.c_int
     for f in (h.oracle_space_fwd, h.oracle_space_bwd, h.oracle_time_fwd, h.oracle_time_bwd,
               h.oracle_time_decode_fwd):
         f.restype = ctypes.c_int
@@ -183,3 +188,39 @@ def bwd(w, q, k, v, dout, scale: float = 0.0, lib=None):
     if w.op == "space":
         return space_bwd(q, k, v, dout, w.agent_begin, w.agent_count, scale, lib=lib)
     return time_bwd(q, k, v, dout, w.window, scale, lib=lib)
+
+
+def rmsnorm_qkv_fwd(x, gamma, w, Hq: int, Hkv: int, D: int, eps: float = 1e-6,
+                    lib: Optional[ctypes.CDLL] = None):
+    """RMS norm (fp64, gain ``gamma``) rounded to bf16, then the QKV projection
+    with weight ``w`` ((Hq+2Hkv)*D, dm).  x is (M, dm).  Returns (q (M, Hq*D),
+    k (M, Hkv*D), v (M, Hkv*D), rstd (M,))."""
+    h = lib or load()
+    x, gamma, w = _f64(x), _f64(gamma), _f64(w)
+    M, dm = x.shape
+    if gamma.shape != (dm,) or w.shape != ((Hq + 2 * Hkv) * D, dm):
+        raise ValueError("shapes x %s gamma %s w %s" % (x.shape, gamma.shape, w.shape))
+    q = np.zeros((M, Hq * D))
+    k = np.zeros((M, Hkv * D))
+    v = np.zeros((M, Hkv * D))
+    rstd = np.zeros(M)
+    _check(h.oracle_rmsnorm_qkv_fwd(M, dm, Hq, Hkv, D, eps, _p(x), _p(gamma), _p(w),
+                                    _p(q), _p(k), _p(v), _p(rstd)), "rmsnorm_qkv_fwd")
+    return q, k, v, rstd
+
+
+def out_proj_fwd(o, w, residual=None, lib: Optional[ctypes.CDLL] = None):
+    """y = residual + o w^T: o (M, din), w (dm, din), residual (M, dm) or None."""
+    h = lib or load()
+    o, w = _f64(o), _f64(w)
+    M, din = o.shape
+    dm = w.shape[0]
+    if w.shape != (dm, din):
+        raise ValueError("w shape %s" % (w.shape,))
+    y = np.zeros((M, dm))
+    res = None if residual is None else _f64(residual)
+    if res is not None and res.shape != (M, dm):
+        raise ValueError("residual shape %s" % (res.shape,))
+    rp = ctypes.cast(None, _DP) if res is None else _p(res)
+    _check(h.oracle_out_proj_fwd(M, dm, din, _p(o), _p(w), rp, _p(y)), "out_proj_fwd")
+    return y

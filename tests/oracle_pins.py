@@ -17,7 +17,10 @@ disagrees with what the mathematics or the pages fix:
   permutes outputs; units are independent;
 * rollout decode: torch SDPA over the ring positions with a mask built from
   the frame each position holds, and row t of time attention over the whole
-  sequence.
+  sequence;
+* projections: torch fp64 ``F.rms_norm``, the bf16 cast and a matmul; the
+  RMS norm's exact invariance to a power-of-two input scale; identity
+  weights.
 """
 from __future__ import annotations
 
@@ -490,10 +493,60 @@ def pin_decode_matches_full_sequence(lib):
             close(lse[:, 0], lse_full[:, t], 1e-12, "decode vs full lse W=%d C=%d t=%d" % (W, C, t))
 
 
+# ---------------------------------------------------------- projections
+
+def pin_rmsnorm_qkv_torch(lib):
+    """RMS norm + bf16 rounding + QKV projection against torch fp64
+    (F.rms_norm, the bf16 cast, a matmul)."""
+    for i, (M, dm, Hq, Hkv, D, eps) in enumerate(((7, 48, 4, 2, 8, 1e-6), (5, 40, 3, 1, 8, 1e-3),
+                                                  (3, 64, 2, 2, 16, 0.0))):
+        x = rnd((M, dm), 610 + i, 3.0)
+        g = rnd((dm,), 620 + i)
+        w = rnd(((Hq + 2 * Hkv) * D, dm), 630 + i, 0.2)
+        q, k, v, rstd = O.rmsnorm_qkv_fwd(x, g, w, Hq, Hkv, D, eps, lib=lib)
+        xt = torch.tensor(x)
+        y = F.rms_norm(xt, (dm,), torch.tensor(g), eps=eps)
+        yb = y.to(torch.bfloat16).to(torch.float64)
+        out = (yb @ torch.tensor(w).T).numpy()
+        close(q, out[:, :Hq * D], 1e-12, "qkv case %d q" % i)
+        close(k, out[:, Hq * D:(Hq + Hkv) * D], 1e-12, "qkv case %d k" % i)
+        close(v, out[:, (Hq + Hkv) * D:], 1e-12, "qkv case %d v" % i)
+        close(rstd, torch.rsqrt((xt * xt).mean(-1) + eps).numpy(), 1e-12, "qkv case %d rstd" % i)
+
+
+def pin_rmsnorm_scale_invariance(lib):
+    """With eps = 0 the RMS norm ignores a power-of-two scale of its input
+    exactly, so every output is bitwise the same."""
+    M, dm, Hq, Hkv, D = 6, 32, 2, 1, 8
+    x = rnd((M, dm), 641)
+    g = rnd((dm,), 642)
+    w = rnd(((Hq + 2 * Hkv) * D, dm), 643)
+    a = O.rmsnorm_qkv_fwd(x, g, w, Hq, Hkv, D, 0.0, lib=lib)
+    b = O.rmsnorm_qkv_fwd(x * 8.0, g, w, Hq, Hkv, D, 0.0, lib=lib)
+    for u, t, n in zip(a[:3], b[:3], "qkv"):
+        close(u, t, 0.0, "scale invariance " + n)
+
+
+def pin_out_proj(lib):
+    """Output projection + residual against a torch fp64 matmul; identity
+    weights return the input plus the residual exactly."""
+    M, din, dm = 9, 24, 16
+    o = rnd((M, din), 651)
+    w = rnd((dm, din), 652)
+    r = rnd((M, dm), 653)
+    y = O.out_proj_fwd(o, w, r, lib=lib)
+    close(y, r + (torch.tensor(o) @ torch.tensor(w).T).numpy(), 1e-12, "out proj")
+    close(O.out_proj_fwd(o, w, None, lib=lib), (torch.tensor(o) @ torch.tensor(w).T).numpy(), 1e-12,
+          "out proj no residual")
+    eye = np.eye(dm, din)
+    close(O.out_proj_fwd(o, eye, r, lib=lib), o[:, :dm] + r, 0.0, "out proj identity")
+
+
 ALL_PINS = [
     pin_sdpa_space, pin_sdpa_time, pin_identical_keys, pin_q_zero_golden, pin_window_one,
     pin_constant_values, pin_backward_sums, pin_finite_differences,
     pin_future_and_window_invariance, pin_agent_invariance, pin_gqa_equals_replicated,
     pin_key_shift, pin_permute_world_tokens, pin_units_independent,
     pin_decode_sdpa, pin_decode_matches_full_sequence,
+    pin_rmsnorm_qkv_torch, pin_rmsnorm_scale_invariance, pin_out_proj,
 ]

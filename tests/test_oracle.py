@@ -57,6 +57,18 @@ MUTANTS = [
     ("decode_query_frame", "const int a = q_frame0 + t;", "const int a = q_frame0 + t + 1;"),
     ("decode_lse", "lse[(((long)b * Tq + t) * N + n) * Hq + h] = m + log(l);",
      "lse[(((long)b * Tq + t) * N + n) * Hq + h] = log(l);"),
+    ("rms_without_mean", "const double r = 1.0 / sqrt(ss / dm + eps);",
+     "const double r = 1.0 / sqrt(ss + eps);"),
+    ("norm_not_rounded", "for (int c = 0; c < dm; ++c) y[c] = round_bf16(xm[c] * r * gamma[c]);",
+     "for (int c = 0; c < dm; ++c) y[c] = xm[c] * r * gamma[c];"),
+    ("gain_dropped", "for (int c = 0; c < dm; ++c) y[c] = round_bf16(xm[c] * r * gamma[c]);",
+     "for (int c = 0; c < dm; ++c) y[c] = round_bf16(xm[c] * r);"),
+    ("qkv_split", "else if (n < nq + nkv) k[m * nkv + (n - nq)] = acc;",
+     "else if (n <= nq + nkv) k[m * nkv + (n - nq) % nkv] = acc;"),
+    ("residual_dropped", "y[m * dm + n] = (residual ? residual[m * dm + n] : 0.0) + dot(",
+     "y[m * dm + n] = 0.0 + dot("),
+    ("out_weight_row", "dot(o + m * din, w + (long)n * din, din);",
+     "dot(o + m * din, w + (long)(n % 2) * din, din);"),
 ]
 
 
