@@ -230,3 +230,51 @@ DECODE_CONFIGS: Dict[str, DecodeWorkload] = {
     "dec_b8": DecodeWorkload("dec_b8", 8, 1, 290, 30, 3, 64, 192, 192, 1000, "bf16", 6001,
                              note="Minecraft rollout, 8 environments"),
 }
+
+
+# --------------------------------------------------- projections beside attention
+
+@dataclass(frozen=True)
+class ProjWorkload:
+    """RMS norm + QKV projection and output projection + residual over M token
+    rows of a d_model-wide residual stream."""
+    name: str
+    M: int
+    d_model: int
+    Hq: int
+    Hkv: int
+    D: int
+    eps: float = 1e-6
+    seed: int = 0
+    note: str = ""
+
+    @property
+    def n_qkv(self) -> int:
+        return (self.Hq + 2 * self.Hkv) * self.D
+
+    def with_(self, **kw) -> "ProjWorkload":
+        return replace(self, **kw)
+
+
+def proj_flops(w: ProjWorkload, which: str) -> float:
+    """2*M*N*K of the GEMM ("qkv" or "out"); the norm is not counted."""
+    if which == "qkv":
+        return 2.0 * w.M * w.n_qkv * w.d_model
+    return 2.0 * w.M * w.d_model * w.Hq * w.D
+
+
+def proj_min_bytes(w: ProjWorkload, which: str) -> float:
+    """qkv: read x, the gain and w_qkv, write q, k, v (and rstd); out: read o,
+    w_o and the residual, write y."""
+    if which == "qkv":
+        return 2.0 * (w.M * w.d_model + w.n_qkv * w.d_model + w.M * w.n_qkv) + 4.0 * (w.d_model + w.M)
+    din = w.Hq * w.D
+    return 2.0 * (w.M * din + w.d_model * din + 2 * w.M * w.d_model)
+
+
+# The dynamics model's layer at 256 frames per GPU: 74,240 token rows (4 x 64
+# blocks of 290 tokens), d_model 1920, 30 / 3 heads of 64.
+PROJ_CONFIGS: Dict[str, ProjWorkload] = {
+    "proj": ProjWorkload("proj", 4 * 64 * 290, 1920, 30, 3, 64, 1e-6, 7000,
+                         note="Minecraft dynamics projections, 256 frames per GPU"),
+}

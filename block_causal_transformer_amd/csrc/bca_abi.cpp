@@ -170,9 +170,78 @@ int do_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, c
   return st;
 }
 
+int validate_proj(const bca_proj_shape* s, bca::ProjDims* d) {
+  if (!s) return fail(BCA_ERR_INVALID_ARG, "projection shape descriptor is NULL");
+  if (s->M <= 0 || s->d_model <= 0 || s->Hq <= 0 || s->Hkv <= 0 || s->D <= 0)
+    return fail(BCA_ERR_INVALID_ARG, "non-positive size (M=%lld d_model=%d Hq=%d Hkv=%d D=%d)",
+                (long long)s->M, s->d_model, s->Hq, s->Hkv, s->D);
+  if (s->d_model % 8 != 0 || s->D % 8 != 0)
+    return fail(BCA_ERR_UNSUPPORTED, "d_model (%d) and D (%d) must be multiples of 8", s->d_model, s->D);
+  if ((double)s->M * (s->d_model > (s->Hq + 2 * s->Hkv) * s->D ? s->d_model : (s->Hq + 2 * s->Hkv) * s->D) > 4.0e15 ||
+      (s->M + 127) / 128 * (((int64_t)(s->Hq + 2 * s->Hkv) * s->D + 127) / 128) > 0x7fffffff ||
+      (int64_t)(s->Hq + 2 * s->Hkv) * s->D > (1 << 30))
+    return fail(BCA_ERR_INVALID_ARG, "projection too large");
+  d->M = s->M;
+  d->d_model = s->d_model;
+  d->Hq = s->Hq;
+  d->Hkv = s->Hkv;
+  d->D = s->D;
+  return BCA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t bca_qkv_workspace_bytes(const bca_proj_shape* shape) {
+  bca::ProjDims d;
+  const std::string saved = g_last_error;
+  if (validate_proj(shape, &d) != BCA_OK) {
+    g_last_error = saved;
+    return 0;
+  }
+  return (size_t)d.M * d.d_model * 2;
+}
+
+int rmsnorm_qkv_fwd(const bca_proj_shape* shape, const void* x, const float* gain, float eps,
+                    const void* w_qkv, void* q, void* k, void* v, float* rstd, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  bca::ProjDims d;
+  int st = validate_proj(shape, &d);
+  if (st) return st;
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(BCA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const char* names[] = {"x", "gain", "w_qkv", "q", "k", "v", "workspace"};
+  const void* ptrs[] = {x, gain, w_qkv, q, k, v, workspace};
+  st = check_ptrs(names, ptrs, 7);
+  if (st) return st;
+  if (rstd && !aligned16(rstd)) return fail(BCA_ERR_INVALID_ARG, "pointer 'rstd' is not 16-byte aligned");
+  const size_t need = (size_t)d.M * d.d_model * 2;
+  if (workspace_bytes < need)
+    return fail(BCA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu required",
+                workspace_bytes, need);
+  hipError_t e = bca::launch_rmsnorm_qkv(d, x, gain, eps, w_qkv, q, k, v, rstd, workspace,
+                                         static_cast<hipStream_t>(stream));
+  st = hip_status(e, "rmsnorm_qkv_fwd launch");
+  if (st == BCA_OK) g_last_error.clear();
+  return st;
+}
+
+int out_proj_fwd(const bca_proj_shape* shape, const void* o, const void* w_o, const void* residual,
+                 void* y, void* stream) {
+  bca::ProjDims d;
+  int st = validate_proj(shape, &d);
+  if (st) return st;
+  const char* names[] = {"o", "w_o", "y"};
+  const void* ptrs[] = {o, w_o, y};
+  st = check_ptrs(names, ptrs, 3);
+  if (st) return st;
+  if (residual && !aligned16(residual))
+    return fail(BCA_ERR_INVALID_ARG, "pointer 'residual' is not 16-byte aligned");
+  hipError_t e = bca::launch_out_proj(d, o, w_o, residual, y, static_cast<hipStream_t>(stream));
+  st = hip_status(e, "out_proj_fwd launch");
+  if (st == BCA_OK) g_last_error.clear();
+  return st;
+}
 
 int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q,
                          const void* k_cache, const void* v_cache, int32_t cache_frames,

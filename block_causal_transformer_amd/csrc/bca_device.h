@@ -81,6 +81,10 @@ __device__ __forceinline__ bf16x8 ld_lds16(const bf16* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+__device__ __forceinline__ void st_global16(bf16* p, const bf16x8& v) {
+  *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
+}
+
 __device__ __forceinline__ void st_lds16(bf16* p, const bf16x8& v) {
   *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
 }

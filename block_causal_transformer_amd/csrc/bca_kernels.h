@@ -52,6 +52,21 @@ hipError_t launch_attn_bwd_generic(const AttnDims& d, const void* q, const void*
                                    const void* dout, void* dq, void* dk, void* dv,
                                    float* delta_ws, hipStream_t stream);
 
+// Projections beside attention: M token rows, d_model features, Hq / Hkv
+// heads of width D.
+struct ProjDims {
+  int64_t M;
+  int d_model, Hq, Hkv, D;
+};
+
+// RMS norm (into `workspace`, M * d_model bf16) then the QKV projection.
+hipError_t launch_rmsnorm_qkv(const ProjDims& d, const void* x, const float* gain, float eps,
+                              const void* w, void* q, void* k, void* v, float* rstd,
+                              void* workspace, hipStream_t stream);
+// y = residual (may be NULL) + o w^T.
+hipError_t launch_out_proj(const ProjDims& d, const void* o, const void* w, const void* residual,
+                           void* y, hipStream_t stream);
+
 // True when the backward of these dims runs on the MFMA kernels (bf16,
 // head_dim 64, any length).
 inline bool bwd_uses_mfma(const AttnDims& d) { return d.dtype == 0 && d.D == 64; }

@@ -1,0 +1,253 @@
+// The projections on either side of attention, bf16 on gfx950 MFMA.
+//
+// Open Dreamer articles (pro.edgex.exchange, fr-FR edition): section
+// "Configuration d'entraînement" (d_model 1920, 30 query heads over 3 KV
+// heads of width 64) and section "Ingénierie de la stabilité", item 3
+// (parameters in fp32, bf16 for most matmul activations and the attention
+// inputs, fp32 for normalization layers).  The norm before the QKV projection
+// is an RMS norm with an fp32 gain whose output, rounded to bf16, is the
+// matmul activation; weights are bf16, stored (out_features, in_features).
+//
+//  rmsnorm_rows_kernel: one wave per token row: fp32 sum of squares, rstd =
+//      1/sqrt(mean + eps), y = bf16(x * rstd * gain) into a workspace.
+//  gemm_nt_kernel: C = A B^T for A (M, K) and B (N, K), both K-contiguous,
+//      fp32 accumulation, bf16 results.  A 128 x 128 output tile per
+//      workgroup of 4 waves (64 x 64 each), K in steps of 64 through
+//      double-buffered LDS (one barrier per step, the next step's tiles
+//      loaded into registers while the current one multiplies).  Each MFMA
+//      forms a tile of C^T (B rows as its A operand) so a lane ends with 4
+//      consecutive columns of one row: one 8-byte store.  Epilogues: the QKV
+//      split (columns [0, nq) to Q, then K, then V, each row-major, which is
+//      the (B,T,N,H,D) layout of the attention inputs) and the residual add.
+#include "bca_device.h"
+#include "bca_kernels.h"
+
+namespace bca {
+
+namespace {
+
+constexpr int GBM = 128, GBN = 128, GBK = 64;
+constexpr int GW = 4;  // waves per workgroup
+
+struct GemmParams {
+  const bf16* a;  // (M, K)
+  const bf16* b;  // (N, K)
+  int64_t M;
+  int N, K;
+  // epilogue 0: columns [0, nq) -> out0 (ld nq), [nq, nq+nkv) -> out1,
+  // [nq+nkv, N) -> out2 (ld nkv).  epilogue 1: out0 (ld N) = C (+ residual)
+  bf16* out0;
+  bf16* out1;
+  bf16* out2;
+  const bf16* residual;
+  int nq, nkv;
+  int mtiles, ntiles;
+};
+
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // [128][64] bf16, 16B chunks xor-swizzled
+  return row * GBK + ((chunk ^ (row & 7)) << 3);
+}
+
+template <int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(GW * 64, GW * 64), amdgpu_waves_per_eu(2, 2)))
+void gemm_nt_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][GBM * GBK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][GBN * GBK];
+
+  int mt, nt;
+  xcd_remap(blockIdx.x, p.mtiles, p.ntiles, mt, nt);
+  const int64_t m0 = (int64_t)mt * GBM;
+  const int n0 = nt * GBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int li = lane & 15, lg = lane >> 4;
+  const int nk = (p.K + GBK - 1) / GBK;
+
+  // global -> register staging: thread t moves 16-byte pieces t + 256 j of
+  // each tile (row = piece / 8, 16-byte column chunk = piece % 8); rows past
+  // M or N read a clamped row and are never stored, columns past K read zero
+  bf16x8 ga[4], gb[4];
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = tid + GW * 64 * j;
+      const int row = piece >> 3, ch = piece & 7;
+      const int k = kt * GBK + ch * 8;
+      const bool kok = k < p.K;
+      const int64_t ar = min(m0 + row, p.M - 1);
+      const int br = min(n0 + row, p.N - 1);
+      const bf16x8 av = ld_global16(p.a + ar * p.K + (kok ? k : 0));
+      const bf16x8 bv = ld_global16(p.b + (int64_t)br * p.K + (kok ? k : 0));
+      ga[j] = kok ? av : zero8();
+      gb[j] = kok ? bv : zero8();
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int piece = tid + GW * 64 * j;
+      const int row = piece >> 3, ch = piece & 7;
+      st_lds16(sA[buf] + tile_off(row, ch), ga[j]);
+      st_lds16(sB[buf] + tile_off(row, ch), gb[j]);
+    }
+  };
+
+  f32x4 acc[4][4];  // [n tile][m tile] of C^T
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  fetch(0);
+  stage(0);
+  if (nk > 1) fetch(1);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const bf16* A = sA[kt & 1];
+    const bf16* Bt = sB[kt & 1];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 bo[4], ao[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bo[t] = ld_lds16(Bt + tile_off(wn * 64 + t * 16 + li, ks * 4 + lg));
+        ao[t] = ld_lds16(A + tile_off(wm * 64 + t * 16 + li, ks * 4 + lg));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(bo[i], ao[j], acc[i][j]);
+    }
+    // the next step's tiles go into the other buffer (last read before the
+    // previous barrier), then the loads for the step after are issued
+    if (kt + 1 < nk) {
+      stage((kt + 1) & 1);
+      if (kt + 2 < nk) fetch(kt + 2);
+    }
+    __syncthreads();
+  }
+
+  // lane (li, lg) of tile (i, j) holds C[m][n .. n+3] with m = row li of the
+  // m tile and n = 4 lg of the n tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t m = m0 + wm * 64 + j * 16 + li;
+    if (m >= p.M) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + wn * 64 + i * 16 + lg * 4;
+      if (n >= p.N) continue;
+      f32x4 c = acc[i][j];
+      if (EPI == 0) {
+        bf16* dst;
+        if (n < p.nq)
+          dst = p.out0 + m * p.nq + n;
+        else if (n < p.nq + p.nkv)
+          dst = p.out1 + m * p.nkv + (n - p.nq);
+        else
+          dst = p.out2 + m * p.nkv + (n - p.nq - p.nkv);
+        *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(c));
+      } else {
+        bf16* dst = p.out0 + m * p.N + n;
+        if (p.residual) {
+          const bf16x4 r = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(p.residual + m * p.N + n));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[e] += (float)r[e];
+        }
+        *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(c));
+      }
+    }
+  }
+}
+
+// One wave per row: fp32 sum of squares over the row, then the scaled,
+// gained values rounded to bf16.  Rows are d_model elements, d_model % 8 == 0.
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const bf16* x, const float* gain, float eps,
+                                                           int64_t M, int dm, bf16* y, float* rstd_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const bf16* xr = x + row * dm;
+  const int nch = dm >> 3;
+  float ss = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    const bf16x8 v = ld_global16(xr + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float f = (float)v[e];
+      ss = __builtin_fmaf(f, f, ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const float r = 1.0f / sqrtf(ss / (float)dm + eps);
+  if (lane == 0 && rstd_out) rstd_out[row] = r;
+  bf16* yr = y + row * dm;
+  for (int c = lane; c < nch; c += 64) {
+    const bf16x8 v = ld_global16(xr + c * 8);
+    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + c * 8);
+    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + c * 8 + 4);
+    f32x4 a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = (float)v[e] * r * g0[e];
+      b[e] = (float)v[4 + e] * r * g1[e];
+    }
+    st_global16(yr + c * 8, pack8(a, b));
+  }
+}
+
+hipError_t launch_gemm(GemmParams& p, int epi, hipStream_t stream) {
+  p.mtiles = (int)((p.M + GBM - 1) / GBM);
+  p.ntiles = (p.N + GBN - 1) / GBN;
+  const int64_t grid = (int64_t)p.mtiles * p.ntiles;
+  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (epi == 0)
+    hipLaunchKernelGGL(gemm_nt_kernel<0>, dim3((unsigned)grid), dim3(GW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_nt_kernel<1>, dim3((unsigned)grid), dim3(GW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_qkv(const ProjDims& d, const void* x, const float* gain, float eps,
+                              const void* w, void* q, void* k, void* v, float* rstd,
+                              void* workspace, hipStream_t stream) {
+  bf16* y = static_cast<bf16*>(workspace);
+  const int64_t blocks = (d.M + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const bf16*>(x), gain, eps, d.M, d.d_model, y, rstd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  GemmParams p{};
+  p.a = y;
+  p.b = static_cast<const bf16*>(w);
+  p.M = d.M;
+  p.N = (d.Hq + 2 * d.Hkv) * d.D;
+  p.K = d.d_model;
+  p.out0 = static_cast<bf16*>(q);
+  p.out1 = static_cast<bf16*>(k);
+  p.out2 = static_cast<bf16*>(v);
+  p.nq = d.Hq * d.D;
+  p.nkv = d.Hkv * d.D;
+  return launch_gemm(p, 0, stream);
+}
+
+hipError_t launch_out_proj(const ProjDims& d, const void* o, const void* w, const void* residual,
+                           void* y, hipStream_t stream) {
+  GemmParams p{};
+  p.a = static_cast<const bf16*>(o);
+  p.b = static_cast<const bf16*>(w);
+  p.M = d.M;
+  p.N = d.d_model;
+  p.K = d.Hq * d.D;
+  p.out0 = static_cast<bf16*>(y);
+  p.residual = static_cast<const bf16*>(residual);
+  return launch_gemm(p, 1, stream);
+}
+
+}  // namespace bca

@@ -28,7 +28,7 @@ from typing import Dict, Optional
 
 import numpy as np
 
-from .configs import DecodeWorkload, Workload
+from .configs import DecodeWorkload, ProjWorkload, Workload
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -117,3 +117,21 @@ def make_decode_inputs(w: DecodeWorkload, variant: int = 0) -> Dict[str, np.ndar
     return {"q": _draw(rq, w.q_shape(), 1.0, w.dtype),
             "k_cache": _draw(rk, w.cache_shape(), 1.0, w.dtype),
             "v_cache": _draw(rv, w.cache_shape(), 1.0, w.dtype)}
+
+
+def make_proj_inputs(w: ProjWorkload, variant: int = 0) -> Dict[str, np.ndarray]:
+    """Inputs of the projections: ``SeedSequence(w.seed + variant)`` spawned into
+    six streams, in order x, gain, w_qkv, o, w_o, residual.  x, o, residual are
+    N(0,1) rounded to bf16; the gain is 1 + N(0, 0.1^2) in fp32; the weights
+    are N(0, 1/in_features) rounded to bf16 (unit-variance outputs)."""
+    ss = np.random.SeedSequence(w.seed + variant)
+    r = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(6)]
+    din = w.Hq * w.D
+    return {
+        "x": _draw(r[0], (w.M, w.d_model), 1.0, "bf16"),
+        "gain": (1.0 + 0.1 * r[1].standard_normal(w.d_model, dtype=np.float32)).astype(np.float32),
+        "w_qkv": _draw(r[2], (w.n_qkv, w.d_model), float(1.0 / np.sqrt(w.d_model)), "bf16"),
+        "o": _draw(r[3], (w.M, din), 1.0, "bf16"),
+        "w_o": _draw(r[4], (w.d_model, din), float(1.0 / np.sqrt(din)), "bf16"),
+        "residual": _draw(r[5], (w.M, w.d_model), 1.0, "bf16"),
+    }

@@ -7,9 +7,11 @@ library is not built, or a call fails, an exception is raised.
 
 Raw entry points carry the C names and arguments:
 ``space_attn_fwd``, ``space_attn_bwd``, ``time_attn_fwd``, ``time_attn_bwd``,
-``time_attn_decode_fwd``, ``bca_bwd_workspace_bytes``, ``bca_status_string``,
+``time_attn_decode_fwd``, ``rmsnorm_qkv_fwd``, ``out_proj_fwd``,
+``bca_bwd_workspace_bytes``, ``bca_qkv_workspace_bytes``, ``bca_status_string``,
 ``bca_last_error``, ``bca_abi_version``.  ``attn_fwd`` / ``attn_bwd`` /
-``attn_decode_fwd`` allocate the outputs with torch and call them.
+``attn_decode_fwd`` / ``qkv_proj`` / ``out_proj`` allocate the outputs with
+torch and call them.
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
 BCA_OK, BCA_ERR_INVALID_ARG, BCA_ERR_UNSUPPORTED, BCA_ERR_HIP = 0, 1, 2, 3
 BCA_BF16, BCA_F32 = 0, 1
 BCA_OP_SPACE, BCA_OP_TIME = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class BcaShape(ctypes.Structure):
@@ -38,6 +40,11 @@ class BcaMask(ctypes.Structure):
                 ("softmax_scale", ctypes.c_float)]
 
 
+class BcaProjShape(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("d_model", ctypes.c_int32), ("Hq", ctypes.c_int32),
+                ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32)]
+
+
 class BcaError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str):
         super().__init__("%s: %s (%s)" % (where, _STATUS.get(status, status), detail))
@@ -49,8 +56,8 @@ _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ["space_attn_fwd", "space_attn_bwd", "time_attn_fwd", "time_attn_bwd",
-            "time_attn_decode_fwd", "bca_bwd_workspace_bytes", "bca_status_string",
-            "bca_last_error", "bca_abi_version"]
+            "time_attn_decode_fwd", "rmsnorm_qkv_fwd", "out_proj_fwd", "bca_bwd_workspace_bytes",
+            "bca_qkv_workspace_bytes", "bca_status_string", "bca_last_error", "bca_abi_version"]
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -76,6 +83,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             f.restype = ctypes.c_int
         h.time_attn_decode_fwd.argtypes = [SP, MP, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P]
         h.time_attn_decode_fwd.restype = ctypes.c_int
+        PP = ctypes.POINTER(BcaProjShape)
+        h.rmsnorm_qkv_fwd.argtypes = [PP, P, P, ctypes.c_float, P, P, P, P, P, P, ctypes.c_size_t, P]
+        h.rmsnorm_qkv_fwd.restype = ctypes.c_int
+        h.out_proj_fwd.argtypes = [PP, P, P, P, P, P]
+        h.out_proj_fwd.restype = ctypes.c_int
+        h.bca_qkv_workspace_bytes.argtypes = [PP]
+        h.bca_qkv_workspace_bytes.restype = ctypes.c_size_t
         h.bca_bwd_workspace_bytes.argtypes = [ctypes.c_int, SP]
         h.bca_bwd_workspace_bytes.restype = ctypes.c_size_t
         h.bca_status_string.argtypes = [ctypes.c_int]
@@ -139,6 +153,21 @@ def time_attn_decode_fwd(shape: BcaShape, mask: BcaMask, q, k_cache, v_cache, ca
     return load().time_attn_decode_fwd(_ref(shape), _ref(mask), _ptr(q), _ptr(k_cache),
                                        _ptr(v_cache), cache_frames, q_frame0, _ptr(o), _ptr(lse),
                                        stream)
+
+
+def rmsnorm_qkv_fwd(shape: BcaProjShape, x, gain, eps: float, w_qkv, q, k, v, rstd, workspace,
+                    workspace_bytes: int, stream=None) -> int:
+    return load().rmsnorm_qkv_fwd(_ref(shape), _ptr(x), _ptr(gain), eps, _ptr(w_qkv), _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(rstd), _ptr(workspace), workspace_bytes,
+                                  stream)
+
+
+def out_proj_fwd(shape: BcaProjShape, o, w_o, residual, y, stream=None) -> int:
+    return load().out_proj_fwd(_ref(shape), _ptr(o), _ptr(w_o), _ptr(residual), _ptr(y), stream)
+
+
+def bca_qkv_workspace_bytes(shape: BcaProjShape) -> int:
+    return int(load().bca_qkv_workspace_bytes(_ref(shape)))
 
 
 def bca_bwd_workspace_bytes(op: int, shape: BcaShape) -> int:
@@ -237,6 +266,45 @@ def attn_decode_fwd(q, k_cache, v_cache, q_frame0: int, window: int = 0, scale: 
     _check(time_attn_decode_fwd(shape, mask, q, k_cache, v_cache, k_cache.shape[1], q_frame0,
                                 o, lse, _stream(stream)), "time_attn_decode_fwd")
     return o, lse
+
+
+def qkv_proj(x, gain, w_qkv, Hq: int, Hkv: int, D: int, eps: float = 1e-6, out=None,
+             workspace=None, stream=None):
+    """RMS norm + QKV projection on torch tensors: x (M, d_model) bf16, gain
+    (d_model) fp32, w_qkv ((Hq+2Hkv)*D, d_model) bf16.  Returns (q (M, Hq*D),
+    k (M, Hkv*D), v (M, Hkv*D), rstd (M,))."""
+    import torch
+    M, dm = x.shape
+    shape = BcaProjShape(M, dm, Hq, Hkv, D)
+    need = bca_qkv_workspace_bytes(shape)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        q = torch.empty((M, Hq * D), dtype=torch.bfloat16, device=x.device)
+        k = torch.empty((M, Hkv * D), dtype=torch.bfloat16, device=x.device)
+        v = torch.empty_like(k)
+        rstd = torch.empty(M, dtype=torch.float32, device=x.device)
+    else:
+        q, k, v, rstd = out
+    _check(rmsnorm_qkv_fwd(shape, x, gain, eps, w_qkv, q, k, v, rstd, workspace,
+                           workspace.numel() * workspace.element_size(), _stream(stream)),
+           "rmsnorm_qkv_fwd")
+    return q, k, v, rstd
+
+
+def out_proj(o, w_o, residual=None, Hq: int = 0, D: int = 0, out=None, stream=None):
+    """y = residual + o w_o^T on torch tensors: o (M, Hq*D), w_o (d_model,
+    Hq*D) bf16, residual (M, d_model) bf16 or None."""
+    import torch
+    M, din = o.shape
+    dm = w_o.shape[0]
+    if not Hq or not D:
+        D = 64 if din % 64 == 0 else 8
+        Hq = din // D
+    shape = BcaProjShape(M, dm, Hq, 1, D)
+    y = torch.empty((M, dm), dtype=torch.bfloat16, device=o.device) if out is None else out
+    _check(out_proj_fwd(shape, o, w_o, residual, y, _stream(stream)), "out_proj_fwd")
+    return y
 
 
 def workload_kwargs(w) -> dict:

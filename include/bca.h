@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define BCA_ABI_VERSION 2
+#define BCA_ABI_VERSION 3
 
 typedef enum {
   BCA_OK = 0,
@@ -157,6 +157,45 @@ int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const voi
  * Delta = rowsum(dO * O) per (query, head), i.e. B*T*N*Hq*4 bytes.  Returns 0
  * for an invalid shape. */
 size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape);
+
+/* ---- projections beside attention ----
+ * Open Dreamer articles (pro.edgex.exchange, fr-FR edition): section
+ * "Configuration d'entraînement" -- d_model 1920, 30 query heads over 3 KV
+ * heads of width 64; section "Ingénierie de la stabilité", item 3 --
+ * parameters in fp32, bf16 for most matmul activations and the attention
+ * inputs, fp32 for normalization layers.  All matrices are row-major bf16;
+ * weights are the bf16 copies stored (out_features, in_features). */
+typedef struct {
+  int64_t M;        /* token rows (B*T*N) */
+  int32_t d_model;  /* model width; multiple of 8 */
+  int32_t Hq, Hkv;  /* query / KV heads */
+  int32_t D;        /* head width; multiple of 8 */
+} bca_proj_shape;
+
+/* Device workspace rmsnorm_qkv_fwd needs: the bf16 normalized activation,
+ * M * d_model * 2 bytes (0 for an invalid shape). */
+size_t bca_qkv_workspace_bytes(const bca_proj_shape* shape);
+
+/* RMS norm then the QKV projection (no biases):
+ *   rstd = 1/sqrt(mean_c x[m][c]^2 + eps),  y = bf16(x * rstd * gain)   (fp32)
+ *   [q | k | v][m] = y[m] w_qkv^T            (bf16 operands, fp32 sums)
+ *   x      (M, d_model) bf16            gain  (d_model) fp32
+ *   w_qkv  ((Hq + 2 Hkv) * D, d_model)  rows: the Q heads, the K heads, the V heads
+ *   q      (M, Hq * D), k, v (M, Hkv * D) bf16: with M = B*T*N these are the
+ *          (B,T,N,H,D) inputs of the attention calls
+ *   rstd   (M) fp32 or NULL (kept for a backward)
+ *   workspace at least bca_qkv_workspace_bytes(shape) bytes.
+ * Errors as for the attention calls; UNSUPPORTED when d_model or D is not a
+ * multiple of 8. */
+int rmsnorm_qkv_fwd(const bca_proj_shape* shape, const void* x, const float* gain, float eps,
+                    const void* w_qkv, void* q, void* k, void* v, float* rstd, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Output projection with the residual add:
+ *   y = residual + o w_o^T    o (M, Hq * D), w_o (d_model, Hq * D),
+ *                             residual (M, d_model) or NULL, y (M, d_model). */
+int out_proj_fwd(const bca_proj_shape* shape, const void* o, const void* w_o, const void* residual,
+                 void* y, void* stream);
 
 /* Static string naming a status code. */
 const char* bca_status_string(int status);
