@@ -27,7 +27,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # per-source device scheduling: the backward kernels interleave better with
 # the scheduler's maximum-ILP strategy (measured ~5% on the dK/dV kernel)
-EXTRA = {"attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+EXTRA = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    # the default scheduler leaves gemm256_kernel's register allocation
+    # copying accumulators between registers on every step
+    "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,

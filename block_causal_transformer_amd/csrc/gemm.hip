@@ -16,9 +16,16 @@
 //      double-buffered LDS (one barrier per step, the next step's tiles
 //      loaded into registers while the current one multiplies).  Each MFMA
 //      forms a tile of C^T (B rows as its A operand) so a lane ends with 4
-//      consecutive columns of one row: one 8-byte store.  Epilogues: the QKV
-//      split (columns [0, nq) to Q, then K, then V, each row-major, which is
-//      the (B,T,N,H,D) layout of the attention inputs) and the residual add.
+//      consecutive columns of one row: one 8-byte store.  Any M, N, K % 8.
+//  gemm256_kernel: the same product with 256 x 256 tiles, one wave per SIMD
+//      holding a 128 x 128 tile in the accumulation registers, K in steps of
+//      64 through two LDS buffers filled by direct-to-LDS loads (no staging
+//      registers), each refilled at mid-step, a step and a half ahead of its
+//      use.  For M % 8 == N % 8 == 0, K % 64 == 0 (the projections of the
+//      1920-wide layers); it halves the LDS operand traffic per MFMA.
+//  Epilogues (both kernels): the QKV split (columns [0, nq) to Q, then K,
+//      then V, each row-major, which is the (B,T,N,H,D) layout of the
+//      attention inputs) and the residual add.
 #include "bca_device.h"
 #include "bca_kernels.h"
 
@@ -28,6 +35,8 @@ namespace {
 
 constexpr int GBM = 128, GBN = 128, GBK = 64;
 constexpr int GW = 4;  // waves per workgroup
+constexpr int GBM2 = 256, GBN2 = 256;  // gemm256_kernel: 2 x 2 waves of 128 x 128
+constexpr int WT = 8;                  // its 16-wide MFMA tiles per wave along m and n
 
 struct GemmParams {
   const bf16* a;  // (M, K)
@@ -44,8 +53,32 @@ struct GemmParams {
   int mtiles, ntiles;
 };
 
-__device__ __forceinline__ int tile_off(int row, int chunk) {  // [128][64] bf16, 16B chunks xor-swizzled
+__device__ __forceinline__ int tile_off(int row, int chunk) {  // [rows][64] bf16, 16B chunks xor-swizzled
   return row * GBK + ((chunk ^ (row & 7)) << 3);
+}
+
+// Stores C[m][n .. n+3] (fp32 c) through epilogue EPI; nothing past M or N.
+template <int EPI>
+__device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f32x4 c) {
+  if (m >= p.M || n >= p.N) return;
+  if (EPI == 0) {
+    bf16* dst;
+    if (n < p.nq)
+      dst = p.out0 + m * p.nq + n;
+    else if (n < p.nq + p.nkv)
+      dst = p.out1 + m * p.nkv + (n - p.nq);
+    else
+      dst = p.out2 + m * p.nkv + (n - p.nq - p.nkv);
+    *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(c));
+  } else {
+    bf16* dst = p.out0 + m * p.N + n;
+    if (p.residual) {
+      const bf16x4 r = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(p.residual + m * p.N + n));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[e] += (float)r[e];
+    }
+    *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(c));
+  }
 }
 
 template <int EPI>
@@ -134,31 +167,136 @@ void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t m = m0 + wm * 64 + j * 16 + li;
-    if (m >= p.M) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = n0 + wn * 64 + i * 16 + lg * 4;
-      if (n >= p.N) continue;
-      f32x4 c = acc[i][j];
-      if (EPI == 0) {
-        bf16* dst;
-        if (n < p.nq)
-          dst = p.out0 + m * p.nq + n;
-        else if (n < p.nq + p.nkv)
-          dst = p.out1 + m * p.nkv + (n - p.nq);
-        else
-          dst = p.out2 + m * p.nkv + (n - p.nq - p.nkv);
-        *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(c));
-      } else {
-        bf16* dst = p.out0 + m * p.N + n;
-        if (p.residual) {
-          const bf16x4 r = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2*>(p.residual + m * p.N + n));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) c[e] += (float)r[e];
-        }
-        *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(c));
-      }
+    for (int i = 0; i < 4; ++i) store4<EPI>(p, m, n0 + wn * 64 + i * 16 + lg * 4, acc[i][j]);
+  }
+}
+
+// 256 x 256 output tile per workgroup of 4 waves, one wave per SIMD: each
+// wave's 128 x 128 tile keeps 64 accumulators (256 registers, the
+// accumulation registers) and reads 16 LDS fragments per 64 MFMAs.  K moves
+// in steps of 64 through two 64 KB LDS buffers filled by direct-to-LDS loads.
+// All LDS reads of a step are issued during its first half, so the buffer is
+// handed back at mid-step (a barrier) and refilled with the step after next
+// there: each step's loads have a step and a half of MFMAs to land in.
+template <int EPI>
+__global__ __attribute__((amdgpu_flat_work_group_size(GW * 64, GW * 64), amdgpu_waves_per_eu(1, 1)))
+void gemm256_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][GBM2 * GBK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][GBN2 * GBK];
+
+  int mt, nt;
+  xcd_remap(blockIdx.x, p.mtiles, p.ntiles, mt, nt);
+  const int64_t m0 = (int64_t)mt * GBM2;
+  const int n0 = nt * GBN2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int li = lane & 15, lg = lane >> 4;
+  const int nk = p.K / GBK;
+
+  // Direct-to-LDS loads (global_load_lds_dwordx4): lane l of one instruction
+  // writes LDS bytes [16 l, 16 l + 16) of a 1 KB block, which is 8 rows of a
+  // 256 x 64 tile in tile_off's layout; lane l takes row l / 8 at chunk
+  // position l % 8, so it loads logical chunk (l % 8) ^ (l / 8) of that row.
+  // M and N are multiples of 8 and K of 64 on this path, so a block of rows
+  // lies wholly inside or wholly past the matrix; one past it loads the last
+  // 8 rows instead, which are never stored.  The block's first row is
+  // uniform (a scalar base address); the lane's byte offset within it is the
+  // same for every block and step.  They are written as inline assembly so
+  // that the compiler, which cannot tell a buffer being filled from one being
+  // read, does not wait for them before every LDS read: the loop waits for
+  // them itself.
+  const int r8 = lane >> 3;
+  const uint32_t loff = (uint32_t)(r8 * p.K + (((lane & 7) ^ r8) << 3)) * 2u;
+  const uint32_t lds_a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&sA[0][0];
+  const uint32_t lds_b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&sB[0][0];
+  auto dma = [&](int kt, int buf, int i) {  // block i < 8 of this wave's share: 2 instructions
+    {
+      const int blk = wave * 8 + i;  // 32 blocks of 8 rows per 256-row tile
+      const int64_t ar = min(m0 + blk * 8, p.M - 8);
+      const int64_t br = min((int64_t)n0 + blk * 8, (int64_t)p.N - 8);
+      const bf16* ga = p.a + ar * p.K + kt * GBK;
+      const bf16* gb = p.b + br * p.K + kt * GBK;
+      const uint32_t la = lds_a + (uint32_t)(buf * GBM2 * GBK + blk * 512) * 2u;
+      const uint32_t lb = lds_b + (uint32_t)(buf * GBN2 * GBK + blk * 512) * 2u;
+      // M0 holds the LDS address; one wait state between writing it and the load
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(loff), "s"(ga), "{m0}"(la) : "memory");
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(loff), "s"(gb), "{m0}"(lb) : "memory");
     }
+  };
+
+  f32x4 acc[WT][WT];  // [n tile][m tile] of C^T
+#pragma unroll
+  for (int i = 0; i < WT; ++i)
+#pragma unroll
+    for (int j = 0; j < WT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // operands of one 32-wide k slice: 8 tiles of B rows, 8 of A rows
+  auto rd_b = [&](int buf, int ks, int t) {
+    return ld_lds16(&sB[buf][0] + tile_off(wn * 128 + t * 16 + li, ks * 4 + lg));
+  };
+  auto rd_a = [&](int buf, int ks, int t) {
+    return ld_lds16(&sA[buf][0] + tile_off(wm * 128 + t * 16 + li, ks * 4 + lg));
+  };
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma(0, 0, i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dma(min(1, nk - 1), 1, i);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // step 0 has landed
+  __syncthreads();
+  // Branches inside a step, where the accumulators are live, make the
+  // register allocator shuffle them, so every step refills: the last two
+  // reload the last step's tiles into a buffer no later step reads.
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    // first half: the first slice's operands, then its 64 MFMAs with the
+    // second slice's reads between them (scheduling fences keep the order)
+    bf16x8 b0[WT], a0[WT], b1[WT], a1[WT];
+#pragma unroll
+    for (int t = 0; t < WT; ++t) a0[t] = rd_a(buf, 0, t);
+#pragma unroll
+    for (int t = 0; t < WT; ++t) b0[t] = rd_b(buf, 0, t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < WT; ++i) {
+#pragma unroll
+      for (int j = 0; j < WT; ++j) acc[i][j] = mfma16(b0[i], a0[j], acc[i][j]);
+      a1[i] = rd_a(buf, 1, i);
+      b1[i] = rd_b(buf, 1, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // mid-step: once every wave's reads of this buffer have completed it
+    // takes the step after next
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // second half: the second slice's MFMAs with the refill's loads spread
+    // between them (a burst of loads would stall the wave's MFMA issue)
+    const int kn = min(kt + 2, nk - 1);
+#pragma unroll
+    for (int i = 0; i < WT; ++i) {
+#pragma unroll
+      for (int j = 0; j < WT; ++j) acc[i][j] = mfma16(b1[i], a1[j], acc[i][j]);
+      dma(kn, buf, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // end of step: the next step's loads (issued before this step's refill)
+    // have landed in every wave
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    __syncthreads();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the surplus reloads land before the workgroup ends
+
+#pragma unroll
+  for (int j = 0; j < WT; ++j) {
+    // one m tile at a time: keeps the residual loads of later tiles from
+    // being hoisted into registers the accumulators still hold
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t m = m0 + wm * 128 + j * 16 + li;
+#pragma unroll
+    for (int i = 0; i < WT; ++i) store4<EPI>(p, m, n0 + wn * 128 + i * 16 + lg * 4, acc[i][j]);
   }
 }
 
@@ -200,14 +338,17 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const bf16* x, const 
 }
 
 hipError_t launch_gemm(GemmParams& p, int epi, hipStream_t stream) {
-  p.mtiles = (int)((p.M + GBM - 1) / GBM);
-  p.ntiles = (p.N + GBN - 1) / GBN;
+  // the lane offset of gemm256_kernel's loads is a 32-bit byte count < 16 K
+  const bool big = p.M >= 8 && p.N >= 8 && p.M % 8 == 0 && p.N % 8 == 0 && p.K % GBK == 0 &&
+                   p.K <= (1 << 24);
+  const int bm = big ? GBM2 : GBM, bn = big ? GBN2 : GBN;
+  p.mtiles = (int)((p.M + bm - 1) / bm);
+  p.ntiles = (p.N + bn - 1) / bn;
   const int64_t grid = (int64_t)p.mtiles * p.ntiles;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (epi == 0)
-    hipLaunchKernelGGL(gemm_nt_kernel<0>, dim3((unsigned)grid), dim3(GW * 64), 0, stream, p);
-  else
-    hipLaunchKernelGGL(gemm_nt_kernel<1>, dim3((unsigned)grid), dim3(GW * 64), 0, stream, p);
+  auto k = big ? (epi == 0 ? gemm256_kernel<0> : gemm256_kernel<1>)
+               : (epi == 0 ? gemm_nt_kernel<0> : gemm_nt_kernel<1>);
+  hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(GW * 64), 0, stream, p);
   return hipGetLastError();
 }
 

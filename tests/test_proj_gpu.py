@@ -1,8 +1,8 @@
 """GPU parity of the projections beside attention (rmsnorm_qkv_fwd,
 out_proj_fwd) against the fp64 oracle, through the C ABI: the dynamics
 layer's widths at a few hundred rows, ragged sizes (rows, features and
-output columns that do not fill a 128 x 128 x 64 tile), and the full 74,240
-rows with the oracle on sampled rows."""
+output columns that do not fill a 128 x 128 x 64 or 256 x 256 x 64 tile),
+and the full 74,240 rows with the oracle on sampled rows."""
 import numpy as np
 import pytest
 
@@ -21,6 +21,13 @@ CASES = {
     "ragged": BASE.with_(M=129, d_model=72, Hq=2, Hkv=1, D=8, seed=7102),
     "mha_k136": BASE.with_(M=257, d_model=136, Hq=4, Hkv=4, D=16, seed=7103),
     "eps_large": BASE.with_(M=64, eps=0.5, seed=7104),
+    # the 256 x 256 tile path (rows and columns multiples of 8, K of 64):
+    # rows that end inside a tile, problems smaller than one tile, and K of
+    # one, two and three 64-wide steps (the loop's prologue and tail)
+    "rows272": BASE.with_(M=272, seed=7105),
+    "rows16_small": BASE.with_(M=16, d_model=128, Hq=2, Hkv=1, D=32, seed=7106),
+    "k64_one_step": BASE.with_(M=48, d_model=64, Hq=1, Hkv=1, D=64, seed=7107),
+    "k192_three_steps": BASE.with_(M=24, d_model=192, Hq=3, Hkv=1, D=64, seed=7108),
 }
 
 
