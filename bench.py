@@ -27,6 +27,13 @@ streaming the generated world frame by frame): space attention of the new
 cache of the 192 frames the window reads (``--decode-batch`` environments at
 once); ``value`` is generated frames per second through that layer pair.
 
+``--workload projections`` times the GEMMs either side of that attention at
+the same 74,240 token rows (section "Configuration d'entraînement": d_model
+1920; section "Ingénierie de la stabilité": fp32 norm, bf16 matmul inputs):
+RMS norm + QKV projection (1920 -> 1920 + 2 x 192) and the output projection
++ residual; ``value`` is their GEMM TFLOP/s (2*M*N*K each, the norm not
+counted).
+
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -46,6 +53,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 TRAFFIC_FILE_DECODE = os.path.join(ROOT, "profiles", "hbm_traffic_rollout_decode.txt")
+TRAFFIC_FILE_PROJ = os.path.join(ROOT, "profiles", "hbm_traffic_projections.txt")
 CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
 
 
@@ -57,13 +65,19 @@ KERNELS = {
     "time_fwd": "attn_fwd_kernel<1>",
     "space_bwd": "attn_bwd_dq_kernel<0> + attn_bwd_dkv_kernel<0>",
     "time_bwd": "attn_bwd_dq_kernel<1> + attn_bwd_dkv_kernel<1>",
+    "qkv_proj": "rmsnorm_rows_kernel + gemm256_kernel<0>",
+    "out_proj": "gemm256_kernel<1>",
 }
 
 
-def source_digest() -> str:
+def source_digest(files=None) -> str:
+    """Digest of the kernel sources ``files`` (names in csrc/; all by default)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
+    for name in sorted(files or os.listdir(CSRC)):
+        path = os.path.join(CSRC, name)
+        if not os.path.exists(path):
+            return ""
+        with open(path, "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -82,7 +96,8 @@ def read_traffic(kernel_key: str, path: str = TRAFFIC_FILE):
                 continue
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha") != source_digest():
+    files = vals.get("source_files")
+    if vals.get("source_sha") != source_digest(files.split(",") if files else None):
         return None
     v = vals.get(kernel_key + ".bytes")
     return float(v) if v else None
@@ -295,6 +310,141 @@ def main_decode(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_proj(w, target_s: float = 15.0):
+    """The fp64 oracle's RMS norm + QKV projection and output projection +
+    residual on a bounded sample of the rows (the full widths), scaled to the
+    same GEMM TFLOP/s unit."""
+    from block_causal_transformer_amd import configs as C, gen
+    from oracle import oracle as O
+
+    def run(n):
+        ws = w.with_(M=n)
+        x = gen.make_proj_inputs(ws)
+        t0 = time.perf_counter()
+        O.rmsnorm_qkv_fwd(x["x"], x["gain"], x["w_qkv"], ws.Hq, ws.Hkv, ws.D, ws.eps)
+        O.out_proj_fwd(x["o"], x["w_o"], x["residual"])
+        dt = time.perf_counter() - t0
+        return dt, C.proj_flops(ws, "qkv") + C.proj_flops(ws, "out")
+
+    dt, _ = run(512)
+    n = max(512, min(w.M, int(512 * target_s / max(dt, 1e-3))))
+    dt, fl = run(n)
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.max_threads(),
+        "kind": "oracle",
+        "sample": "%d token rows (d_model %d, %d q / %d kv heads of %d): RMS norm + QKV projection "
+                  "and output projection + residual, fp64, %.1f s" % (n, w.d_model, w.Hq, w.Hkv, w.D, dt),
+    }
+
+
+def main_proj(args):
+    import torch
+    from block_causal_transformer_amd import configs as C, gen, ops
+
+    if not os.path.exists(ops.LIB_PATH):
+        from block_causal_transformer_amd import build as hip_build
+        hip_build.build()
+    ops.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = C.PROJ_CONFIGS["proj"]
+    x = gen.make_proj_inputs(w)
+    bf = torch.bfloat16
+    d = {k: torch.from_numpy(v).to(dev) for k, v in x.items()}
+    del x
+    for k in ("x", "w_qkv", "o", "w_o", "residual"):
+        d[k] = d[k].to(bf)
+    shape = ops.BcaProjShape(w.M, w.d_model, w.Hq, w.Hkv, w.D)
+    q = torch.empty((w.M, w.Hq * w.D), dtype=bf, device=dev)
+    k = torch.empty((w.M, w.Hkv * w.D), dtype=bf, device=dev)
+    v = torch.empty_like(k)
+    rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
+    ws_bytes = ops.bca_qkv_workspace_bytes(shape)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    y = torch.empty((w.M, w.d_model), dtype=bf, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def qkv():
+        if ops.rmsnorm_qkv_fwd(shape, d["x"], d["gain"], w.eps, d["w_qkv"], q, k, v, rstd, ws,
+                               ws_bytes, sp):
+            raise RuntimeError(ops.bca_last_error())
+
+    def out():
+        if ops.out_proj_fwd(shape, d["o"], d["w_o"], d["residual"], y, sp):
+            raise RuntimeError(ops.bca_last_error())
+
+    seq = (("qkv_proj", qkv), ("out_proj", out))
+    for _ in range(args.warmup):
+        for _, fn in seq:
+            fn()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(seq) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        evs[s_][0].record(stream)
+        for i, (_, fn) in enumerate(seq):
+            fn()
+            evs[s_][i + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ops_ = {}
+    total = 0.0
+    for i, (name, _) in enumerate(seq):
+        which = "qkv" if name == "qkv_proj" else "out"
+        ms = sum(evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)) / args.steps
+        fl, by = C.proj_flops(w, which), C.proj_min_bytes(w, which)
+        total += fl
+        ops_[name] = {"ms": round(ms, 5), "tflops": round(fl / ms / 1e9, 2),
+                      "pct_mfma_peak": round(100.0 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                      "gbps": round(by / ms / 1e6, 1), "flop": fl, "min_bytes": by}
+    # the roofline is quoted on the output projection's GEMM: one launch per
+    # call, so its event time is the kernel's duration (the QKV call also
+    # runs the norm kernel)
+    dm = ops_["out_proj"]
+    roof = roofline_of(dm["flop"], dm["min_bytes"], dm["ms"])
+    roof["kernel"] = "out_proj (" + KERNELS["out_proj"] + ")"
+    roof["traffic"] = read_traffic("out_proj", TRAFFIC_FILE_PROJ)
+    out_ = {
+        "metric": "projection GEMM TFLOP/s beside the attention (QKV with RMS norm, output with "
+                  "residual) and % of MI355X bf16 MFMA peak",
+        "value": round(total * args.steps / elapsed / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Minecraft dynamics layer projections at 256 frames per GPU: RMS norm + QKV "
+                        "projection (74,240 rows, 1920 -> 1920 + 2 x 192) and output projection "
+                        "(1920 -> 1920) + residual",
+            "M": w.M, "d_model": w.d_model, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "eps": w.eps,
+            "flop_per_step": total,
+        },
+        "pct_mfma_peak": round(100.0 * total * args.steps / elapsed / 1e12 / PEAK_BF16_TFLOPS, 2),
+        "ops": {k_: {kk: vv for kk, vv in v_.items() if kk not in ("flop", "min_bytes")}
+                for k_, v_ in ops_.items()},
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_proj(w),
+    }
+    print(json.dumps(out_), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,7 +453,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
-    ap.add_argument("--workload", choices=("train_step", "tokenizer_step", "long_time", "rollout_decode"),
+    ap.add_argument("--workload", choices=("train_step", "tokenizer_step", "long_time", "rollout_decode",
+                                           "projections"),
                     default="train_step")
     ap.add_argument("--decode-batch", type=int, default=1,
                     help="rollout_decode: environments generated at once")
@@ -316,6 +467,8 @@ def main():
         if args.steps == 30 and args.warmup == 5:
             args.steps, args.warmup = 200, 20
         return main_decode(args)
+    if args.workload == "projections":
+        return main_proj(args)
 
     return main_step(args)
 

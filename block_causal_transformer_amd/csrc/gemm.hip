@@ -211,19 +211,37 @@ void gemm256_kernel(GemmParams p) {
   const uint32_t loff = (uint32_t)(r8 * p.K + (((lane & 7) ^ r8) << 3)) * 2u;
   const uint32_t lds_a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&sA[0][0];
   const uint32_t lds_b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&sB[0][0];
-  auto dma = [&](int kt, int buf, int i) {  // block i < 8 of this wave's share: 2 instructions
-    {
-      const int blk = wave * 8 + i;  // 32 blocks of 8 rows per 256-row tile
-      const int64_t ar = min(m0 + blk * 8, p.M - 8);
-      const int64_t br = min((int64_t)n0 + blk * 8, (int64_t)p.N - 8);
-      const bf16* ga = p.a + ar * p.K + kt * GBK;
-      const bf16* gb = p.b + br * p.K + kt * GBK;
-      const uint32_t la = lds_a + (uint32_t)(buf * GBM2 * GBK + blk * 512) * 2u;
-      const uint32_t lb = lds_b + (uint32_t)(buf * GBN2 * GBK + blk * 512) * 2u;
-      // M0 holds the LDS address; one wait state between writing it and the load
-      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(loff), "s"(ga), "{m0}"(la) : "memory");
-      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(loff), "s"(gb), "{m0}"(lb) : "memory");
+  // A wave fills 8 consecutive 1 KB blocks of each tile.  The instruction's
+  // offset field moves both the LDS destination and the global address, so
+  // one M0 value (the wave's 8 KB span + 4 KB) serves all 8 blocks with
+  // offsets -4096 .. 3072; each block's scalar base is lowered by its offset.
+  // (Rewriting M0 before every load measurably stalls the issuing wave.)
+  // dma(kt, buf, q) loads blocks 2q, 2q + 1 of A (q < 4) or of B (q >= 4).
+  auto dma = [&](int kt, int buf, int q) {
+    const bool isb = q >= 4;
+    const int i0 = (q & 3) * 2;
+    const int blk0 = wave * 8 + i0;
+    const int64_t lim = isb ? (int64_t)p.N - 8 : p.M - 8;
+    const int64_t r0 = min((isb ? (int64_t)n0 : m0) + blk0 * 8, lim);
+    const int64_t r1 = min((isb ? (int64_t)n0 : m0) + blk0 * 8 + 8, lim);
+    const bf16* src = isb ? p.b : p.a;
+    const int off0 = i0 * 1024 - 4096;
+    const char* g0 = reinterpret_cast<const char*>(src + r0 * p.K + kt * GBK) - off0;
+    const char* g1 = reinterpret_cast<const char*>(src + r1 * p.K + kt * GBK) - (off0 + 1024);
+    const uint32_t m0v = (isb ? lds_b : lds_a) + (uint32_t)(buf * GBM2 * GBK + wave * 8 * 512) * 2u + 4096u;
+    // one wait state between writing M0 and the first load
+#define BCA_DMA2(O0, O1)                                                                        \
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:" #O0                          \
+               "\n\tglobal_load_lds_dwordx4 %0, %2 offset:" #O1 ::"v"(loff), "s"(g0), "s"(g1), \
+               "{m0}"(m0v)                                                                      \
+               : "memory")
+    switch (q & 3) {
+      case 0: BCA_DMA2(-4096, -3072); break;
+      case 1: BCA_DMA2(-2048, -1024); break;
+      case 2: BCA_DMA2(0, 1024); break;
+      default: BCA_DMA2(2048, 3072); break;
     }
+#undef BCA_DMA2
   };
 
   f32x4 acc[WT][WT];  // [n tile][m tile] of C^T
@@ -241,9 +259,9 @@ void gemm256_kernel(GemmParams p) {
   };
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma(0, 0, i);
+  for (int q = 0; q < 8; ++q) dma(0, 0, q);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dma(min(1, nk - 1), 1, i);
+  for (int q = 0; q < 8; ++q) dma(min(1, nk - 1), 1, q);
   asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // step 0 has landed
   __syncthreads();
   // Branches inside a step, where the accumulators are live, make the

@@ -3,15 +3,16 @@
     python -m block_causal_transformer_amd.rocprof_summary stats \\
         KERNEL_STATS_CSV OUT_MD --cmd "the profiled command"
     python -m block_causal_transformer_amd.rocprof_summary traffic \\
-        FETCH_COUNTER_CSV WRITE_COUNTER_CSV OUT_TXT --cmd "..."
+        FETCH_COUNTER_CSV WRITE_COUNTER_CSV OUT_TXT --cmd "..." --sources a.hip,b.h
 
 ``stats`` lists every kernel of a ``--kernel-trace --stats`` run (calls,
 average and total duration).  ``traffic`` reads two ``--pmc FETCH_SIZE`` /
 ``--pmc WRITE_SIZE`` runs of ``bench.py --copy-probe-mib M`` and writes HBM
-bytes per launch of each attention op, each counter scaled by the factor
+bytes per launch of each op, each counter scaled by the factor
 that makes it read the known byte count of the plain device copy of M MiB
 that the same run performs; ``bench.py`` reads that file for the roofline's
-``traffic`` field (and ignores it once the kernel sources change).
+``traffic`` field (and ignores it once one of the ``--sources`` files the
+kernels are built from changes).
 """
 from __future__ import annotations
 
@@ -26,7 +27,8 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
 
-# attention op of each kernel (template argument 0 = space, 1 = time)
+# op of each kernel (attention: template argument 0 = space, 1 = time, 2 =
+# decode; projections: 0 = QKV split, 1 = output + residual)
 OPS = [
     (r"attn_fwd_kernel<2>", "time_decode"),
     (r"attn_fwd_kernel<0>", "space_fwd"),
@@ -35,12 +37,19 @@ OPS = [
     (r"attn_bwd_dkv_kernel<0>", "space_bwd"),
     (r"attn_bwd_dq_kernel<1>", "time_bwd"),
     (r"attn_bwd_dkv_kernel<1>", "time_bwd"),
+    (r"rmsnorm_rows_kernel", "qkv_proj"),
+    (r"gemm256_kernel<0>", "qkv_proj"),
+    (r"gemm_nt_kernel<0>", "qkv_proj"),
+    (r"gemm256_kernel<1>", "out_proj"),
+    (r"gemm_nt_kernel<1>", "out_proj"),
 ]
+OP_ORDER = ("space_fwd", "space_bwd", "time_fwd", "time_bwd", "time_decode", "qkv_proj", "out_proj")
 
 
-def source_digest() -> str:
+def source_digest(files=None) -> str:
+    """Digest of the kernel sources ``files`` (names in csrc/; all by default)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(files or os.listdir(CSRC)):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -80,9 +89,9 @@ def cmd_stats(args):
         op = op_of(r["Name"])
         if op:
             per_op[op] += float(r["AverageNs"]) / 1e3
-    out += ["", "Average duration per attention op (sum over its kernels):", "",
+    out += ["", "Average duration per op (sum over its kernels):", "",
             "| op | average (us) |", "|---|---|"]
-    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd", "time_decode"):
+    for op in OP_ORDER:
         if op in per_op:
             out.append("| %s | %.1f |" % (op, per_op[op]))
     out.append("")
@@ -127,7 +136,8 @@ def cmd_traffic(args):
            "#   " + args.cmd.replace("COUNTER", "WRITE_SIZE"),
            "# Each counter (KiB per dispatch) is scaled by the factor that makes it",
            "# read %d bytes for the plain %d MiB device copy in the same run." % (probe, args.copy_mib),
-           "source_sha=%s" % source_digest(),
+           "source_files=%s" % ",".join(sorted(args.sources.split(","))),
+           "source_sha=%s" % source_digest(args.sources.split(",")),
            "copy_probe_bytes=%d" % probe]
     for cname, (ck, fac, _) in vals.items():
         out.append("%s.copy_kib=%.1f" % (cname.lower(), ck))
@@ -138,7 +148,7 @@ def cmd_traffic(args):
             avg = sum(vs) / len(vs)
             out.append("%s.%s.kib_per_dispatch=%.1f  # %s" % (op, cname.lower(), avg, kname))
             ops[op] += avg * 1024.0 * fac
-    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd", "time_decode"):
+    for op in OP_ORDER:
         if op in ops:
             out.append("%s.bytes=%.0f" % (op, ops[op]))
     out.append("")
@@ -160,6 +170,9 @@ def main(argv=None):
     b.add_argument("out")
     b.add_argument("--cmd", required=True)
     b.add_argument("--copy-mib", type=int, default=2048)
+    b.add_argument("--sources", required=True,
+                   help="comma-separated csrc/ files the profiled kernels are built from; the "
+                        "summary is taken as stale once any of them changes")
     args = ap.parse_args(argv)
     if args.what == "stats":
         cmd_stats(args)

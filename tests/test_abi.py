@@ -184,3 +184,69 @@ def test_decode_rejects_bad_arguments(lib):
     assert decode_call(good_shape(T=1, D=48), mask, 4, 3) == ops.BCA_ERR_UNSUPPORTED
     assert decode_call(good_shape(T=2), mask, 8, 2 ** 31 - 1) == ops.BCA_ERR_INVALID_ARG
     assert "overflows" in ops.bca_last_error()
+
+
+def proj_shape(M=300, d_model=1920, Hq=30, Hkv=3, D=64):
+    return ops.BcaProjShape(M, d_model, Hq, Hkv, D)
+
+
+def qkv_call(shape, eps=1e-6, ptrs=None, rstd=None, ws_bytes=None):
+    p = ptrs or [FAKE] * 7
+    need = ops.bca_qkv_workspace_bytes(shape) if ws_bytes is None else ws_bytes
+    return ops.rmsnorm_qkv_fwd(shape, p[0], p[1], eps, p[2], p[3], p[4], p[5], rstd, p[6], need)
+
+
+def test_projection_workspace_query(lib):
+    assert ops.bca_qkv_workspace_bytes(proj_shape()) == 300 * 1920 * 2
+    assert ops.bca_qkv_workspace_bytes(proj_shape(M=0)) == 0
+    assert ops.bca_qkv_workspace_bytes(proj_shape(d_model=100)) == 0
+    assert ops.bca_qkv_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("field,value", [("M", 0), ("M", -3), ("d_model", 0), ("Hq", 0),
+                                         ("Hkv", -1), ("D", 0)])
+def test_projection_non_positive_sizes(lib, field, value):
+    s = proj_shape(**{field: value})
+    assert qkv_call(s, ws_bytes=1 << 20) == ops.BCA_ERR_INVALID_ARG
+    assert "non-positive" in ops.bca_last_error()
+    assert ops.out_proj_fwd(s, FAKE, FAKE, None, FAKE) == ops.BCA_ERR_INVALID_ARG
+
+
+def test_projection_widths_must_be_multiples_of_8(lib):
+    assert qkv_call(proj_shape(d_model=1916), ws_bytes=1 << 30) == ops.BCA_ERR_UNSUPPORTED
+    assert "multiples of 8" in ops.bca_last_error()
+    assert ops.out_proj_fwd(proj_shape(D=60), FAKE, FAKE, None, FAKE) == ops.BCA_ERR_UNSUPPORTED
+
+
+def test_projection_rejects_bad_arguments(lib):
+    s = proj_shape()
+    assert ops.rmsnorm_qkv_fwd(None, FAKE, FAKE, 1e-6, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30) \
+        == ops.BCA_ERR_INVALID_ARG
+    for eps in (-1e-3, float("nan"), float("inf")):
+        assert qkv_call(s, eps=eps) == ops.BCA_ERR_INVALID_ARG
+        assert "eps" in ops.bca_last_error()
+    names = ("x", "gain", "w_qkv", "q", "k", "v", "workspace")
+    for i, name in enumerate(names):
+        p = [FAKE] * 7
+        p[i] = 0
+        assert qkv_call(s, ptrs=p) == ops.BCA_ERR_INVALID_ARG
+        assert name in ops.bca_last_error() and "NULL" in ops.bca_last_error()
+        p[i] = FAKE + 8
+        assert qkv_call(s, ptrs=p) == ops.BCA_ERR_INVALID_ARG
+        assert "aligned" in ops.bca_last_error()
+    assert qkv_call(s, rstd=FAKE + 4) == ops.BCA_ERR_INVALID_ARG
+    assert "rstd" in ops.bca_last_error()
+    rc = qkv_call(s, ws_bytes=ops.bca_qkv_workspace_bytes(s) - 1)
+    assert rc == ops.BCA_ERR_INVALID_ARG and "workspace" in ops.bca_last_error()
+    for i, name in enumerate(("o", "w_o", "y")):
+        p = [FAKE] * 3
+        p[i] = 0
+        assert ops.out_proj_fwd(s, p[0], p[1], None, p[2]) == ops.BCA_ERR_INVALID_ARG
+        assert name in ops.bca_last_error()
+    assert ops.out_proj_fwd(s, FAKE, FAKE, FAKE + 2, FAKE) == ops.BCA_ERR_INVALID_ARG
+    assert "residual" in ops.bca_last_error()
+
+
+def test_projection_too_large(lib):
+    assert qkv_call(proj_shape(M=2 ** 40), ws_bytes=2 ** 62) == ops.BCA_ERR_INVALID_ARG
+    assert "too large" in ops.bca_last_error()
