@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build", "obj")
 ASM = os.path.join(ROOT, "_build", "asm")
 LIB = os.path.join(PKG, "libbca.so")
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_generic.hip", "gemm.hip", "bca_abi.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_generic.hip", "attn_short.hip", "gemm.hip", "bca_abi.cpp"]
 ARCH = os.environ.get("BCA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -102,8 +102,9 @@ int do_fwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
   st = check_ptrs(names, ptrs, 5);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = bca::fwd_uses_mfma(d) ? bca::launch_attn_fwd_bf16(d, q, k, v, o, lse, s)
-                                       : bca::launch_attn_fwd_generic(d, q, k, v, o, lse, s);
+  hipError_t e = bca::uses_short(d)      ? bca::launch_attn_fwd_short(d, q, k, v, o, lse, s)
+                  : bca::fwd_uses_mfma(d) ? bca::launch_attn_fwd_bf16(d, q, k, v, o, lse, s)
+                                          : bca::launch_attn_fwd_generic(d, q, k, v, o, lse, s);
   st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_fwd launch" : "time_attn_fwd launch");
   if (st == BCA_OK) g_last_error.clear();
   return st;
@@ -128,7 +129,10 @@ int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
       return fail(BCA_ERR_INVALID_ARG, "workspace is NULL or not 16-byte aligned");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = bca::bwd_uses_mfma(d)
+  // the short kernels form Delta per row themselves and leave the workspace alone
+  hipError_t e = bca::uses_short(d)
+                     ? bca::launch_attn_bwd_short(d, q, k, v, o, lse, dout, dq, dk, dv, s)
+                 : bca::bwd_uses_mfma(d)
                      ? bca::launch_attn_bwd_bf16(d, q, k, v, o, lse, dout, dq, dk, dv, workspace, s)
                      : bca::launch_attn_bwd_generic(d, q, k, v, o, lse, dout, dq, dk, dv,
                                                     static_cast<float*>(workspace), s);

@@ -67,6 +67,19 @@ hipError_t launch_rmsnorm_qkv(const ProjDims& d, const void* x, const float* gai
 hipError_t launch_out_proj(const ProjDims& d, const void* o, const void* w, const void* residual,
                            void* y, hipStream_t stream);
 
+// Short problems (bf16, head_dim 64, space or time op with at most 32 key
+// positions and at most 64 folded query rows): one wave per problem.
+hipError_t launch_attn_fwd_short(const AttnDims& d, const void* q, const void* k, const void* v,
+                                 void* o, float* lse, hipStream_t stream);
+hipError_t launch_attn_bwd_short(const AttnDims& d, const void* q, const void* k, const void* v,
+                                 const void* o, const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, hipStream_t stream);
+inline bool uses_short(const AttnDims& d) {
+  if (d.dtype != 0 || d.D != 64 || (d.op != 0 && d.op != 1)) return false;
+  const int L = d.op == 0 ? d.N : d.T;
+  return L <= 32 && L * (d.Hq / d.Hkv) <= 64;
+}
+
 // True when the backward of these dims runs on the MFMA kernels (bf16,
 // head_dim 64, any length).
 inline bool bwd_uses_mfma(const AttnDims& d) { return d.dtype == 0 && d.D == 64; }

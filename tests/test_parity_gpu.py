@@ -96,6 +96,17 @@ RAGGED += [
     C.Workload("time_T1024_W192", "time", 1, 1024, 2, 6, 2, 64, "bf16", 192, 0, 0, 1.0, 9013),
     C.Workload("time_T700_W0", "time", 1, 700, 1, 6, 2, 64, "bf16", 0, 0, 0, 1.0, 9014),
     C.Workload("time_T650_W333", "time", 1, 650, 2, 3, 1, 64, "bf16", 333, 0, 0, 1.0, 9015),
+    # short problems (at most 32 keys and 64 folded rows: one wave per
+    # problem), one case per (rows, keys) instance, and the MFMA kernels just
+    # past that limit
+    C.Workload("short_space_N10_mha", "space", 1, 3, 10, 3, 3, 64, "bf16", 0, 0, 0, 1.0, 9020),
+    C.Workload("short_time_T32_W8", "time", 1, 32, 3, 2, 2, 64, "bf16", 8, 0, 0, 1.0, 9021),
+    C.Workload("short_time_T6_G10", "time", 2, 6, 3, 30, 3, 64, "bf16", 192, 0, 0, 1.0, 9022),
+    C.Workload("short_space_N16_G4", "space", 1, 2, 16, 8, 2, 64, "bf16", 0, 15, 1, 1.0, 9023),
+    C.Workload("short_time_T32_G2_W0", "time", 1, 32, 2, 4, 2, 64, "bf16", 0, 0, 0, 1.0, 9024),
+    C.Workload("short_space_N21_G3_agent_mid", "space", 2, 2, 21, 9, 3, 64, "bf16", 0, 5, 3, 1.0, 9025),
+    C.Workload("mfma_space_N33", "space", 1, 2, 33, 6, 2, 64, "bf16", 0, 32, 1, 1.0, 9026),
+    C.Workload("mfma_time_T33_W8", "time", 1, 33, 2, 2, 2, 64, "bf16", 8, 0, 0, 1.0, 9027),
 ]
 
 
