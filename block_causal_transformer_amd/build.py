@@ -29,6 +29,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # the scheduler's maximum-ILP strategy (measured ~5% on the dK/dV kernel)
 EXTRA = {
     "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    # fmaxf on values that are never NaN: without this every operand of a
+    # row maximum is first canonicalized (one extra v_max per score)
+    "attn_fwd.hip": ["-fno-honor-nans"],
     # the default scheduler leaves gemm256_kernel's register allocation
     # copying accumulators between registers on every step
     "gemm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],

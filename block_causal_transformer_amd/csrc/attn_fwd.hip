@@ -199,6 +199,12 @@ void attn_fwd_kernel(FwdParams p) {
             sc[qt][h] = mfma16(k1, qreg[qt][1], z);
           }
         }
+        // hipcc leaves as few as 7 wait states between these MFMAs and the
+        // first VALU read of sc along the branch paths below (8 are needed);
+        // a fixed pad covers every path
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         if (!tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
           // a select, not a conditional store: hipcc dropped conditional
           // element stores into this array of vectors
