@@ -598,6 +598,11 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   splits = max(1, min(splits, (chunks + DQ_W - 1) / DQ_W));
   int per = (chunks + splits - 1) / splits;
   per = ((per + DQ_W - 1) / DQ_W) * DQ_W;
+  // Windowed time attention over many frames: fewer rows per workgroup, so
+  // that the keys a workgroup sees fit one LDS block (otherwise every pass
+  // restages all its blocks).
+  if (d.op == OP_TIME && p.window > 0)
+    while (per > DQ_W && time_wg_key_span(p.L, p.G, p.window, (long)per * DQ_QC) > KMAX) per -= DQ_W;
   p.rows_per_split = per * DQ_QC;
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
   const long g1 = problems * p.splits;

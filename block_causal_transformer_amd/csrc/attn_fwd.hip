@@ -333,6 +333,11 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   splits = max(1, min(splits, (chunks + FW - 1) / FW));
   int per = (chunks + splits - 1) / splits;
   per = ((per + FW - 1) / FW) * FW;  // whole passes of FW chunks
+  // Windowed time attention over many frames: fewer rows per workgroup, so
+  // that the keys a workgroup sees fit one LDS block (otherwise every pass
+  // restages all its blocks).
+  if (d.op == OP_TIME && p.window > 0)
+    while (per > FW && time_wg_key_span(p.L, p.G, p.window, (long)per * QCH) > KMAX) per -= FW;
   p.rows_per_split = per * QCH;
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
   const long grid = problems * p.splits;

@@ -29,6 +29,21 @@ inline void decode_key_range(const AttnDims& d, int& first, int& last) {
   first = (d.window > 0 && d.q_frame0 - d.window + 1 > 0) ? d.q_frame0 - d.window + 1 : 0;
 }
 
+// Time attention split into workgroups of `rows_per_wg` folded rows (G per
+// position): the largest number of key positions one workgroup can see,
+// counting the 32-key alignment of its first key (window W > 0, L frames).
+inline int time_wg_key_span(int L, int G, int W, long rows_per_wg) {
+  const long rows = (long)L * G;
+  int span = 0;
+  for (long r0 = 0; r0 < rows; r0 += rows_per_wg) {
+    const long r1 = r0 + rows_per_wg < rows ? r0 + rows_per_wg : rows;
+    const int p0 = (int)(r0 / G), p1 = (int)((r1 - 1) / G);
+    const int k0 = (p0 - W + 1 > 0 ? p0 - W + 1 : 0) & ~31;
+    if (p1 + 1 - k0 > span) span = p1 + 1 - k0;
+  }
+  return span;
+}
+
 // Keys per LDS block of the MFMA backward: the dq kernel streams longer
 // problems through LDS in blocks of this many keys, and the dkv kernel gives
 // every such block its own workgroup.
