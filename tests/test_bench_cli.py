@@ -1,0 +1,47 @@
+"""bench.py host logic that needs no GPU: the one-GPU guard, the roofline
+figures and the reading of committed counter summaries."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_roofline_bound_follows_the_ridge():
+    ridge = bench.PEAK_BF16_TFLOPS * 1e12 / (bench.PEAK_HBM_GBPS * 1e9)  # FLOP per byte
+    # above the ridge: MFMA-bound, achieved in TFLOP/s
+    r = bench.roofline_of(2e12, 2e12 / (2 * ridge), 2.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["achieved"] == pytest.approx(1000.0) and r["frac"] == pytest.approx(0.4)
+    # below: HBM-bound, achieved in GB/s
+    r = bench.roofline_of(1e9, 1e9, 0.5)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["achieved"] == pytest.approx(2000.0) and r["frac"] == pytest.approx(0.25)
+
+
+def test_traffic_summary_is_used_only_for_the_sources_it_was_taken_on(tmp_path):
+    files = ["gemm.hip", "bca_device.h"]
+    good = tmp_path / "good.txt"
+    good.write_text("# comment\nsource_files=%s\nsource_sha=%s\nout_proj.bytes=12345\n"
+                    % (",".join(files), bench.source_digest(files)))
+    assert bench.read_traffic("out_proj", str(good)) == 12345.0
+    assert bench.read_traffic("qkv_proj", str(good)) is None
+    stale = tmp_path / "stale.txt"
+    stale.write_text("source_files=%s\nsource_sha=0000\nout_proj.bytes=1\n" % ",".join(files))
+    assert bench.read_traffic("out_proj", str(stale)) is None
+    assert bench.read_traffic("out_proj", str(tmp_path / "missing.txt")) is None
+    # a file that names a source that no longer exists is stale
+    gone = tmp_path / "gone.txt"
+    gone.write_text("source_files=no_such.hip\nsource_sha=%s\nout_proj.bytes=1\n" % bench.source_digest(files))
+    assert bench.read_traffic("out_proj", str(gone)) is None
