@@ -8,8 +8,9 @@
 // is an RMS norm with an fp32 gain whose output, rounded to bf16, is the
 // matmul activation; weights are bf16, stored (out_features, in_features).
 //
-//  rmsnorm_rows_kernel: one wave per token row: fp32 sum of squares, rstd =
-//      1/sqrt(mean + eps), y = bf16(x * rstd * gain) into a workspace.
+//  rmsnorm_rows_kernel: one wave per token row (held in registers up to
+//      2048 features): fp32 sum of squares, rstd = 1/sqrt(mean + eps),
+//      y = bf16(x * rstd * gain) into a workspace.
 //  gemm_nt_kernel: C = A B^T for A (M, K) and B (N, K), both K-contiguous,
 //      fp32 accumulation, bf16 results.  A 128 x 128 output tile per
 //      workgroup of 4 waves (64 x 64 each), K in steps of 64 through
@@ -319,30 +320,46 @@ void gemm256_kernel(GemmParams p) {
 }
 
 // One wave per row: fp32 sum of squares over the row, then the scaled,
-// gained values rounded to bf16.  Rows are d_model elements, d_model % 8 == 0.
+// gained values rounded to bf16.  Rows are d_model elements, d_model % 8 ==
+// 0.  Rows of up to 64 * 8 * RC elements stay in registers between the two
+// passes (one read of x); longer rows are read twice.
+template <int RC>
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const bf16* x, const float* gain, float eps,
                                                            int64_t M, int dm, bf16* y, float* rstd_out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   const bf16* xr = x + row * dm;
+  bf16* yr = y + row * dm;
   const int nch = dm >> 3;
+  bf16x8 held[RC];
   float ss = 0.f;
-  for (int c = lane; c < nch; c += 64) {
-    const bf16x8 v = ld_global16(xr + c * 8);
+  if (nch <= 64 * RC) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float f = (float)v[e];
-      ss = __builtin_fmaf(f, f, ss);
+    for (int i = 0; i < RC; ++i) {
+      const int c = lane + 64 * i;
+      held[i] = c < nch ? ld_global16(xr + c * 8) : zero8();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)held[i][e];
+        ss = __builtin_fmaf(f, f, ss);
+      }
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) {
+      const bf16x8 v = ld_global16(xr + c * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float f = (float)v[e];
+        ss = __builtin_fmaf(f, f, ss);
+      }
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
   const float r = 1.0f / sqrtf(ss / (float)dm + eps);
   if (lane == 0 && rstd_out) rstd_out[row] = r;
-  bf16* yr = y + row * dm;
-  for (int c = lane; c < nch; c += 64) {
-    const bf16x8 v = ld_global16(xr + c * 8);
+  auto put = [&](int c, const bf16x8& v) {
     const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + c * 8);
     const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + c * 8 + 4);
     f32x4 a, b;
@@ -352,6 +369,15 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const bf16* x, const 
       b[e] = (float)v[4 + e] * r * g1[e];
     }
     st_global16(yr + c * 8, pack8(a, b));
+  };
+  if (nch <= 64 * RC) {
+#pragma unroll
+    for (int i = 0; i < RC; ++i) {
+      const int c = lane + 64 * i;
+      if (c < nch) put(c, held[i]);
+    }
+  } else {
+    for (int c = lane; c < nch; c += 64) put(c, ld_global16(xr + c * 8));
   }
 }
 
@@ -378,7 +404,7 @@ hipError_t launch_rmsnorm_qkv(const ProjDims& d, const void* x, const float* gai
   bf16* y = static_cast<bf16*>(workspace);
   const int64_t blocks = (d.M + 3) / 4;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(rmsnorm_rows_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<const bf16*>(x), gain, eps, d.M, d.d_model, y, rstd);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -28,6 +28,8 @@ CASES = {
     "rows16_small": BASE.with_(M=16, d_model=128, Hq=2, Hkv=1, D=32, seed=7106),
     "k64_one_step": BASE.with_(M=48, d_model=64, Hq=1, Hkv=1, D=64, seed=7107),
     "k192_three_steps": BASE.with_(M=24, d_model=192, Hq=3, Hkv=1, D=64, seed=7108),
+    # rows wider than the norm kernel keeps in registers (2048 features)
+    "wide_rows": BASE.with_(M=40, d_model=2304, Hq=4, Hkv=2, D=64, seed=7109),
 }
 
 
