@@ -18,7 +18,8 @@
 //      loaded into registers while the current one multiplies).  Each MFMA
 //      forms a tile of C^T (B rows as its A operand) so a lane ends with 4
 //      consecutive columns of one row: one 8-byte store.  Any M, N, K % 8.
-//  gemm256_kernel: the same product with 256 x 256 tiles, one wave per SIMD
+//  gemm256_kernel: the same product with 256 x 256 tiles (256 x 192 when N
+//      is a multiple of 192 but not of 256), one wave per SIMD
 //      holding a 128 x 128 tile in the accumulation registers, K in steps of
 //      64 through two LDS buffers filled by direct-to-LDS loads (no staging
 //      registers), each refilled at mid-step, a step and a half ahead of its
@@ -173,23 +174,30 @@ void gemm_nt_kernel(GemmParams p) {
   }
 }
 
-// 256 x 256 output tile per workgroup of 4 waves, one wave per SIMD: each
-// wave's 128 x 128 tile keeps 64 accumulators (256 registers, the
-// accumulation registers) and reads 16 LDS fragments per 64 MFMAs.  K moves
+// 256 x (32 WTN) output tile per workgroup of 4 waves, one wave per SIMD:
+// each wave's 128 x 16 WTN tile keeps 8 WTN accumulators (up to all 256
+// accumulation registers) and reads 8 + WTN LDS fragments per 8 WTN MFMAs.
+// WTN = 8 (256 columns) in general; WTN = 6 (192 columns) when N is a
+// multiple of 192 but not of 256 (the 1920-wide output projection: 10 full
+// column tiles instead of 7.5).  K moves
 // in steps of 64 through two 64 KB LDS buffers filled by direct-to-LDS loads.
 // All LDS reads of a step are issued during its first half, so the buffer is
 // handed back at mid-step (a barrier) and refilled with the step after next
 // there: each step's loads have a step and a half of MFMAs to land in.
-template <int EPI>
+template <int EPI, int WTN>
 __global__ __attribute__((amdgpu_flat_work_group_size(GW * 64, GW * 64), amdgpu_waves_per_eu(1, 1)))
 void gemm256_kernel(GemmParams p) {
+  constexpr int BN = 32 * WTN;     // tile columns
+  constexpr int NBP = WTN / 2;     // block pairs of B per wave and step
+  constexpr int NLD = 2 * (4 + NBP);  // load instructions per wave and step
+  static_assert(WTN == 8 || WTN == 6, "tile widths of this kernel");
   __shared__ __attribute__((aligned(16))) bf16 sA[2][GBM2 * GBK];
-  __shared__ __attribute__((aligned(16))) bf16 sB[2][GBN2 * GBK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][BN * GBK];
 
   int mt, nt;
   xcd_remap(blockIdx.x, p.mtiles, p.ntiles, mt, nt);
   const int64_t m0 = (int64_t)mt * GBM2;
-  const int n0 = nt * GBN2;
+  const int n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -212,16 +220,17 @@ void gemm256_kernel(GemmParams p) {
   const uint32_t loff = (uint32_t)(r8 * p.K + (((lane & 7) ^ r8) << 3)) * 2u;
   const uint32_t lds_a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&sA[0][0];
   const uint32_t lds_b = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16*)&sB[0][0];
-  // A wave fills 8 consecutive 1 KB blocks of each tile.  The instruction's
-  // offset field moves both the LDS destination and the global address, so
-  // one M0 value (the wave's 8 KB span + 4 KB) serves all 8 blocks with
-  // offsets -4096 .. 3072; each block's scalar base is lowered by its offset.
-  // (Rewriting M0 before every load measurably stalls the issuing wave.)
-  // dma(kt, buf, q) loads blocks 2q, 2q + 1 of A (q < 4) or of B (q >= 4).
+  // A wave fills 8 consecutive 1 KB blocks of the A tile and WTN of the B
+  // tile.  The instruction's offset field moves both the LDS destination and
+  // the global address, so one M0 value (the wave's span + 4 KB) serves all of
+  // a tile's blocks with offsets -4096 .. 3072; each block's scalar base is
+  // lowered by its offset.  (Rewriting M0 before every load measurably stalls
+  // the issuing wave.)  dma(kt, buf, q) loads blocks 2q, 2q + 1 of A (q < 4)
+  // or 2(q - 4), 2(q - 4) + 1 of B (4 <= q < 4 + NBP).
   auto dma = [&](int kt, int buf, int q) {
     const bool isb = q >= 4;
     const int i0 = (q & 3) * 2;
-    const int blk0 = wave * 8 + i0;
+    const int blk0 = wave * (isb ? WTN : 8) + i0;
     const int64_t lim = isb ? (int64_t)p.N - 8 : p.M - 8;
     const int64_t r0 = min((isb ? (int64_t)n0 : m0) + blk0 * 8, lim);
     const int64_t r1 = min((isb ? (int64_t)n0 : m0) + blk0 * 8 + 8, lim);
@@ -229,7 +238,8 @@ void gemm256_kernel(GemmParams p) {
     const int off0 = i0 * 1024 - 4096;
     const char* g0 = reinterpret_cast<const char*>(src + r0 * p.K + kt * GBK) - off0;
     const char* g1 = reinterpret_cast<const char*>(src + r1 * p.K + kt * GBK) - (off0 + 1024);
-    const uint32_t m0v = (isb ? lds_b : lds_a) + (uint32_t)(buf * GBM2 * GBK + wave * 8 * 512) * 2u + 4096u;
+    const uint32_t m0v = isb ? lds_b + (uint32_t)(buf * BN * GBK + wave * WTN * 512) * 2u + 4096u
+                             : lds_a + (uint32_t)(buf * GBM2 * GBK + wave * 8 * 512) * 2u + 4096u;
     // one wait state between writing M0 and the first load
 #define BCA_DMA2(O0, O1)                                                                        \
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:" #O0                          \
@@ -245,25 +255,25 @@ void gemm256_kernel(GemmParams p) {
 #undef BCA_DMA2
   };
 
-  f32x4 acc[WT][WT];  // [n tile][m tile] of C^T
+  f32x4 acc[WTN][WT];  // [n tile][m tile] of C^T
 #pragma unroll
-  for (int i = 0; i < WT; ++i)
+  for (int i = 0; i < WTN; ++i)
 #pragma unroll
     for (int j = 0; j < WT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // operands of one 32-wide k slice: 8 tiles of B rows, 8 of A rows
+  // operands of one 32-wide k slice: WTN tiles of B rows, 8 of A rows
   auto rd_b = [&](int buf, int ks, int t) {
-    return ld_lds16(&sB[buf][0] + tile_off(wn * 128 + t * 16 + li, ks * 4 + lg));
+    return ld_lds16(&sB[buf][0] + tile_off(wn * 16 * WTN + t * 16 + li, ks * 4 + lg));
   };
   auto rd_a = [&](int buf, int ks, int t) {
     return ld_lds16(&sA[buf][0] + tile_off(wm * 128 + t * 16 + li, ks * 4 + lg));
   };
 
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma(0, 0, q);
+  for (int q = 0; q < 4 + NBP; ++q) dma(0, 0, q);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) dma(min(1, nk - 1), 1, q);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // step 0 has landed
+  for (int q = 0; q < 4 + NBP; ++q) dma(min(1, nk - 1), 1, q);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");  // step 0 has landed
   __syncthreads();
   // Branches inside a step, where the accumulators are live, make the
   // register allocator shuffle them, so every step refills: the last two
@@ -272,18 +282,22 @@ void gemm256_kernel(GemmParams p) {
     const int buf = kt & 1;
     // first half: the first slice's operands, then its 64 MFMAs with the
     // second slice's reads between them (scheduling fences keep the order)
-    bf16x8 b0[WT], a0[WT], b1[WT], a1[WT];
+    bf16x8 b0[WTN], a0[WT], b1[WTN], a1[WT];
 #pragma unroll
     for (int t = 0; t < WT; ++t) a0[t] = rd_a(buf, 0, t);
 #pragma unroll
-    for (int t = 0; t < WT; ++t) b0[t] = rd_b(buf, 0, t);
+    for (int t = 0; t < WTN; ++t) b0[t] = rd_b(buf, 0, t);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
+    for (int i = 0; i < WTN; ++i) {
 #pragma unroll
       for (int j = 0; j < WT; ++j) acc[i][j] = mfma16(b0[i], a0[j], acc[i][j]);
       a1[i] = rd_a(buf, 1, i);
       b1[i] = rd_b(buf, 1, i);
+      if (i == WTN - 1) {
+#pragma unroll
+        for (int t = WTN; t < WT; ++t) a1[t] = rd_a(buf, 1, t);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // mid-step: once every wave's reads of this buffer have completed it
@@ -295,15 +309,19 @@ void gemm256_kernel(GemmParams p) {
     // between them (a burst of loads would stall the wave's MFMA issue)
     const int kn = min(kt + 2, nk - 1);
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
+    for (int i = 0; i < WTN; ++i) {
 #pragma unroll
       for (int j = 0; j < WT; ++j) acc[i][j] = mfma16(b1[i], a1[j], acc[i][j]);
       dma(kn, buf, i);
+      if (i == WTN - 1) {
+#pragma unroll
+        for (int q = WTN; q < 4 + NBP; ++q) dma(kn, buf, q);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // end of step: the next step's loads (issued before this step's refill)
     // have landed in every wave
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
     __syncthreads();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the surplus reloads land before the workgroup ends
@@ -315,7 +333,7 @@ void gemm256_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     const int64_t m = m0 + wm * 128 + j * 16 + li;
 #pragma unroll
-    for (int i = 0; i < WT; ++i) store4<EPI>(p, m, n0 + wn * 128 + i * 16 + lg * 4, acc[i][j]);
+    for (int i = 0; i < WTN; ++i) store4<EPI>(p, m, n0 + wn * 16 * WTN + i * 16 + lg * 4, acc[i][j]);
   }
 }
 
@@ -385,13 +403,15 @@ hipError_t launch_gemm(GemmParams& p, int epi, hipStream_t stream) {
   // the lane offset of gemm256_kernel's loads is a 32-bit byte count < 16 K
   const bool big = p.M >= 8 && p.N >= 8 && p.M % 8 == 0 && p.N % 8 == 0 && p.K % GBK == 0 &&
                    p.K <= (1 << 24);
-  const int bm = big ? GBM2 : GBM, bn = big ? GBN2 : GBN;
+  const bool n192 = big && p.N % 192 == 0 && p.N % 256 != 0;
+  const int bm = big ? GBM2 : GBM, bn = n192 ? 192 : big ? GBN2 : GBN;
   p.mtiles = (int)((p.M + bm - 1) / bm);
   p.ntiles = (p.N + bn - 1) / bn;
   const int64_t grid = (int64_t)p.mtiles * p.ntiles;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
-  auto k = big ? (epi == 0 ? gemm256_kernel<0> : gemm256_kernel<1>)
-               : (epi == 0 ? gemm_nt_kernel<0> : gemm_nt_kernel<1>);
+  auto k = n192  ? (epi == 0 ? gemm256_kernel<0, 6> : gemm256_kernel<1, 6>)
+           : big ? (epi == 0 ? gemm256_kernel<0, 8> : gemm256_kernel<1, 8>)
+                 : (epi == 0 ? gemm_nt_kernel<0> : gemm_nt_kernel<1>);
   hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(GW * 64), 0, stream, p);
   return hipGetLastError();
 }
