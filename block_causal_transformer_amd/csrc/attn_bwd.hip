@@ -148,8 +148,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
   // Per chunk, this lane's query column in each of the two 16-column tiles
   // (padding columns read a real, clamped row and are never stored).
   struct ChunkIn {
-    bf16x8 q[2][2], d[2][2], o[2][2];
-    float lse[2];
+    bf16x8 q[2][2], d[2][2];
+    float lse[2], delta[2];
   };
   auto load_chunk = [&](int ch, ChunkIn& in) {
     const int r0c = row0 + ch * DQ_QC;
@@ -163,9 +163,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
       for (int s = 0; s < 2; ++s) {
         in.q[qt][s] = ld_global16(p.q + off + s * 32);
         in.d[qt][s] = ld_global16(p.dout + off + s * 32);
-        in.o[qt][s] = ld_global16(p.o + off + s * 32);
       }
       in.lse[qt] = p.lse[gl.base + (int64_t)pos * gl.pos_stride + g * G + hq];
+      in.delta[qt] = p.delta[gl.base + (int64_t)pos * gl.pos_stride + g * G + hq];
     }
   };
   // one chunk per wave and pass; with several key blocks, every block is
@@ -191,15 +191,12 @@ void attn_bwd_dq_kernel(BwdParams p) {
         const int rr = min(r, row1 - 1);
         qpos[qt] = row_pos(rr, p.inv_g);
         hh[qt] = rr - qpos[qt] * G;
-        float part = 0.f;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           qreg[qt][s] = nxt.q[qt][s];
           dreg[qt][s] = nxt.d[qt][s];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) part = __builtin_fmaf((float)nxt.d[qt][s][e], (float)nxt.o[qt][s][e], part);
         }
-        dlt[qt] = group4_sum(part);
+        dlt[qt] = nxt.delta[qt];
         lse2[qt] = qv[qt] ? nxt.lse[qt] * kLog2e : INFINITY;
       }
 #pragma unroll
@@ -283,12 +280,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
       }
     }
     if (!active) continue;
-    // Delta is stored only now so that no wait on the store delays the
-    // first products of the chunk
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       if (!qv[qt]) continue;
-      if (lg == 0) p.delta[gl.base + (int64_t)qpos[qt] * gl.pos_stride + g * G + hh[qt]] = dlt[qt];
       bf16* dst = p.dq + gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 4;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -398,9 +392,10 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   // stalls on a global load a chunk early.
   const bool carries_q = tid < 256;
   const int srow = (tid & 255) >> 3, sch = tid & 7;
-  bf16x8 pre = zero8();
+  bf16x8 pre = zero8(), pre_o = zero8();
   float pre_s = 0.f;
   bool pre_valid = false;
+  int64_t pre_lo = 0;
   auto fetch = [&](int c) {
     // padding rows read a real (clamped) row; their LSE of +inf zeroes P
     const int r = c * KV_QC + srow;
@@ -411,15 +406,31 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + sch * 8;
     const int64_t lo = gl.base + (int64_t)pos * gl.pos_stride + g * G + hh;
     pre = ld_global16((carries_q ? p.q : p.dout) + off);
-    pre_s = carries_q ? p.lse[lo] : p.delta[lo];
+    if (carries_q)
+      pre_s = p.lse[lo];
+    else
+      pre_o = ld_global16(p.o + off);
+    pre_lo = lo;
   };
+  // Delta = rowsum(dO * O) is formed here, from the 8 pieces of a row held by
+  // 8 adjacent threads, and written to the workspace for the dq kernel (which
+  // runs after this one); workgroups whose chunk ranges overlap write the
+  // same bits
   auto stage = [&](KvBuf& b) {
     st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
-    if (sch == 0) {
-      if (carries_q)
-        b.lse[srow] = pre_valid ? pre_s * kLog2e : INFINITY;
-      else
-        b.delta[srow] = pre_s;
+    if (carries_q) {
+      if (sch == 0) b.lse[srow] = pre_valid ? pre_s * kLog2e : INFINITY;
+    } else {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t = __builtin_fmaf((float)pre[e], (float)pre_o[e], t);
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      t += __shfl_xor(t, 4, 64);
+      if (sch == 0) {
+        b.delta[srow] = t;
+        if (pre_valid) p.delta[pre_lo] = t;
+      }
     }
   };
 
@@ -614,11 +625,11 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 
   if (d.op == OP_SPACE) {
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<OP_SPACE>, dim3((unsigned)g2), dim3(KV_W * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_dkv_kernel<OP_TIME>, dim3((unsigned)g2), dim3(KV_W * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   }
   return hipGetLastError();
 }
