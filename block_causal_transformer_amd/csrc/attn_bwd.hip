@@ -18,21 +18,21 @@
 // Two kernels, each keeping one side of the problem stationary in registers
 // so that no sum crosses waves (no atomics; bitwise deterministic):
 //
+//  dkv kernel (key-parallel, launched first): each wave owns 16-key tiles
+//             of one problem and keeps their dK^T, dV^T accumulators and K, V
+//             operands in registers; the problem's query rows stream through
+//             LDS in 32-row chunks (double-buffered, prefetched into registers
+//             one chunk ahead): S = Q K^T and dP = dO V^T, then dV^T += dO^T P
+//             and dK^T += Q^T dS on MFMA, with the Q^T and dO^T operands read
+//             straight from the row-major chunk by transposing LDS reads.
+//             Staging a chunk also forms its rows' Delta from dO and O, which
+//             it leaves in the workspace for the second kernel.
 //  dq kernel  (query-parallel, laid out like the forward): a workgroup holds
 //             K, V and K^T of one (unit, KV head) problem in LDS; each wave
 //             owns 32 query rows (position x head-in-group) and sweeps the
 //             visible keys in 32-key steps: S^T = K Q^T and dP^T = V dO^T on
 //             MFMA (every lane holds one query column), P^T and dS^T on VALU,
-//             dQ^T += K^T dS^T on MFMA.  It also forms Delta from O and dO
-//             and leaves it in the workspace for the second kernel.
-//  dkv kernel (key-parallel): each wave owns 16-key tiles of one problem and
-//             keeps their dK^T, dV^T accumulators and K, V operands in
-//             registers; the problem's query rows stream through LDS in
-//             32-row chunks (double-buffered, prefetched into registers one
-//             chunk ahead): S = Q K^T and dP = dO V^T, then dV^T += dO^T P
-//             and dK^T += Q^T dS on MFMA, with the Q^T and dO^T operands
-//             read straight from the row-major chunk by transposing LDS
-//             reads.
+//             dQ^T += K^T dS^T on MFMA.
 //
 // Key steps (dq) and query chunks (dkv) that the causal / window ranges make
 // invisible are never visited.  The split costs two more matmul passes than a
