@@ -38,9 +38,9 @@ OPS = [
     (r"attn_bwd_dq_kernel<1>", "time_bwd"),
     (r"attn_bwd_dkv_kernel<1>", "time_bwd"),
     (r"rmsnorm_rows_kernel", "qkv_proj"),
-    (r"gemm256_kernel<0>", "qkv_proj"),
+    (r"gemm256_kernel<0[,>]", "qkv_proj"),
     (r"gemm_nt_kernel<0>", "qkv_proj"),
-    (r"gemm256_kernel<1>", "out_proj"),
+    (r"gemm256_kernel<1[,>]", "out_proj"),
     (r"gemm_nt_kernel<1>", "out_proj"),
 ]
 OP_ORDER = ("space_fwd", "space_bwd", "time_fwd", "time_bwd", "time_decode", "qkv_proj", "out_proj")
@@ -67,7 +67,7 @@ def short_name(kernel: str) -> str:
 def op_of(kernel: str):
     k = short_name(kernel)
     for pat, op in OPS:
-        if k.startswith(pat):
+        if re.match(pat, k):
             return op
     return None
 
