@@ -294,7 +294,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------ dkv kernel
 
 constexpr int KV_W = 8;    // waves per workgroup
-constexpr int KV_TPW = 3;  // 16-key tile slots per wave (tile = wave + 8 * slot)
+constexpr int KV_TPW = 3;  // most 16-key tile slots per wave (tile = wave + 8 * slot)
 constexpr int KV_QC = 32;  // query rows per chunk
 
 __device__ __forceinline__ int row_off(int row, int chunk) {  // [32][64]
@@ -310,12 +310,20 @@ __device__ __forceinline__ int tr_piece_off(int h, int dt, int li, int lg) {
   return row * 64 + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
 }
 
+// One DPP lane move (row_mask and bank_mask all set).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 struct KvBuf {
   bf16 Q[KV_QC * 64];
   bf16 dO[KV_QC * 64];
   float lse[KV_QC];
   float delta[KV_QC];
 };
+// the lane offsets below add 16 rows as 2048 bytes and reach dO from Q
+static_assert(offsetof(KvBuf, dO) == KV_QC * 64 * 2, "KvBuf layout");
 
 // One workgroup per (unit, KV head) problem.  Each wave keeps the K and V
 // rows of its tiles (the B operands of S and dP) and their dK^T, dV^T
@@ -328,7 +336,7 @@ struct KvBuf {
 // an agent row iff agent_begin*G <= r < (agent_begin + agent_count)*G.
 // Keys past the end only feed their own (discarded) dK, dV columns here, so
 // they need no mask.
-template <int OP>
+template <int OP, int TPW>
 __global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) KvBuf sbuf[2];
@@ -353,12 +361,12 @@ void attn_bwd_dkv_kernel(BwdParams p) {
 
   // K and V operands of the wave's tiles, straight from global memory
   // (keys past the end read as zero)
-  bf16x8 KB[KV_TPW][2], VB[KV_TPW][2];
-  int keyG[KV_TPW];    // time: key * G
-  bool kagent[KV_TPW];  // space: the lane's key is an agent key
-  bool keyok[KV_TPW];
+  bf16x8 KB[TPW][2], VB[TPW][2];
+  int keyG[TPW];    // time: key * G
+  bool kagent[TPW];  // space: the lane's key is an agent key
+  bool keyok[TPW];
 #pragma unroll
-  for (int m = 0; m < KV_TPW; ++m) {
+  for (int m = 0; m < TPW; ++m) {
     const int key = kb0 + (wave + KV_W * m) * 16 + li;
     const bool ok = key < kend;
     const int64_t off = gk.base + (int64_t)min(key, p.L - 1) * gk.pos_stride + g * 64;
@@ -373,13 +381,15 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     kagent[m] = (unsigned)(key - p.agent_begin) < (unsigned)p.agent_count;
     keyok[m] = ok;
   }
-  const unsigned winG = p.window > 0 ? (unsigned)(p.window * G) : 0xffffffffu;
+  // time: key k is visible to folded row r iff 0 <= r - k*G < winG (no
+  // window: the whole sequence, so the test still rejects r < k*G)
+  const unsigned winG = (unsigned)((p.window > 0 ? p.window : p.L) * G);
   const int agentG0 = p.agent_begin * G;
   const unsigned agentGn = (unsigned)(p.agent_count * G);
 
-  f32x4 dKT[KV_TPW][4], dVT[KV_TPW][4];
+  f32x4 dKT[TPW][4], dVT[TPW][4];
 #pragma unroll
-  for (int m = 0; m < KV_TPW; ++m)
+  for (int m = 0; m < TPW; ++m)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       dKT[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -424,9 +434,11 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       float t = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) t = __builtin_fmaf((float)pre[e], (float)pre_o[e], t);
-      t += __shfl_xor(t, 1, 64);
-      t += __shfl_xor(t, 2, 64);
-      t += __shfl_xor(t, 4, 64);
+      // sum over the 8 lanes of the row: quad swaps (1 0 3 2), (2 3 0 1),
+      // then the half-row mirror pairs each quad with the other one
+      t += dpp_f32<0xB1>(t);
+      t += dpp_f32<0x4E>(t);
+      t += dpp_f32<0x141>(t);
       if (sch == 0) {
         b.delta[srow] = t;
         if (pre_valid) p.delta[pre_lo] = t;
@@ -445,6 +457,20 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     }
   }
   const int nchunks = c_hi;
+
+  // byte offsets of this lane's LDS reads within a chunk buffer, formed once
+  // and kept in registers (the 16-row half, dO and the buffer are added as
+  // constants): row-major reads of rows li (+16), column chunks s*4 + lg,
+  // and the transposing reads of column slice dt
+  int offQ[2], offT[4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) offQ[s] = row_off(li, s * 4 + lg) * 2;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) offT[dt] = tr_piece_off(0, dt, li, lg) * 2;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) asm volatile("" : "+v"(offQ[s]));
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) asm volatile("" : "+v"(offT[dt]));
   fetch(c_lo);
   stage(sbuf[c_lo & 1]);
   if (c_lo + 1 < nchunks) fetch(c_lo + 1);
@@ -452,14 +478,15 @@ void attn_bwd_dkv_kernel(BwdParams p) {
 
   for (int c = c_lo; c < nchunks; ++c) {
     KvBuf& b = sbuf[c & 1];
+    const char* bb = reinterpret_cast<const char*>(&b);
     const int r0 = c * KV_QC;
     const int qlo = r0 / G;
     const int qhi = (min(r0 + KV_QC, p.rows) - 1) / G;
     const bool world_rows = !(qlo >= p.agent_begin && qhi < p.agent_begin + p.agent_count);
-    bool work[KV_TPW], edge[KV_TPW];
+    bool work[TPW], edge[TPW];
     bool anyw = false;
 #pragma unroll
-    for (int m = 0; m < KV_TPW; ++m) {
+    for (int m = 0; m < TPW; ++m) {
       const int t = wave + KV_W * m;
       const int k0 = kb0 + t * 16, k1 = min(k0 + 16, kend);
       work[m] = t < nkt && !tile_none_visible(md, qlo, qhi, k0, k1);
@@ -469,55 +496,80 @@ void attn_bwd_dkv_kernel(BwdParams p) {
         edge[m] = world_rows && p.agent_count > 0 && k0 < p.agent_begin + p.agent_count && k1 > p.agent_begin;
       anyw |= work[m];
     }
-    bf16x8 Pb[KV_TPW], dSb[KV_TPW];
+    bf16x8 Pb[TPW], dSb[TPW];
     if (anyw) {
-      // 1. S and dP for the owned tiles, then P and dS as packed B operands,
-      // one 16-row half of the chunk at a time
-      bf16x4 Ph[KV_TPW][2], dSh[KV_TPW][2];
+      // 1. S and dP for the owned tiles, then P and dS as packed B operands;
+      // both 16-row halves of the chunk go through a tile together, so that
+      // each tile carries two independent MFMA / exp chains
+      bf16x4 Ph[TPW][2], dSh[TPW][2];
+      bf16x8 Qa[2][2], dOa[2][2];
+      f32x4 lse4[2], ndl4[2];
+      auto load_stats = [&]() {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
+          ndl4[qt] = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
+        }
+      };
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
-        bf16x8 Qa[2], dOa[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          Qa[s] = ld_lds16(b.Q + row_off(qt * 16 + li, s * 4 + lg));
-          dOa[s] = ld_lds16(b.dO + row_off(qt * 16 + li, s * 4 + lg));
+          Qa[qt][s] = ld_lds16(reinterpret_cast<const bf16*>(bb + offQ[s] + qt * 2048));
+          dOa[qt][s] = ld_lds16(reinterpret_cast<const bf16*>(bb + offQ[s] + qt * 2048 + KV_QC * 128));
         }
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
-        const f32x4 ndl4 = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
-        const int rb = r0 + qt * 16 + lg * 4;  // folded row of element j = rb + j
+      }
+      if constexpr (TPW < 3) load_stats();
+      const int rb = r0 + lg * 4;  // folded row of element j of half qt: rb + 16 qt + j
 #pragma unroll
-        for (int m = 0; m < KV_TPW; ++m) {
-          if (!work[m]) continue;
-          f32x4 S = {0.f, 0.f, 0.f, 0.f};
-          S = mfma16(Qa[0], KB[m][0], S);
-          S = mfma16(Qa[1], KB[m][1], S);
-          // the accumulator starts at -Delta, so it ends at dP - Delta
-          f32x4 dP = ndl4;
-          dP = mfma16(dOa[0], VB[m][0], dP);
-          dP = mfma16(dOa[1], VB[m][1], dP);
-          f32x4 P;
+      for (int m = 0; m < TPW; ++m) {
+        if (!work[m]) continue;
+        if constexpr (TPW >= 3) {
+          // with three tiles the row statistics are read again for every
+          // tile rather than held across the loop (register pressure)
+          asm volatile("" ::: "memory");
+          load_stats();
+        }
+        f32x4 S[2], dP[2], P[2];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) P[j] = fast_exp2(__builtin_fmaf(S[j], p.scale_log2, -lse4[j]));
-          if (edge[m]) {
+        for (int qt = 0; qt < 2; ++qt) {
+          S[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          S[qt] = mfma16(Qa[qt][0], KB[m][0], S[qt]);
+          S[qt] = mfma16(Qa[qt][1], KB[m][1], S[qt]);
+        }
+        // the accumulator starts at -Delta, so it ends at dP - Delta
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          dP[qt] = mfma16(dOa[qt][0], VB[m][0], ndl4[qt]);
+          dP[qt] = mfma16(dOa[qt][1], VB[m][1], dP[qt]);
+        }
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) P[qt][j] = fast_exp2(__builtin_fmaf(S[qt][j], p.scale_log2, -lse4[qt][j]));
+        if (edge[m]) {
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               bool vis;
               if (OP == OP_TIME)
-                vis = (unsigned)(rb + j - keyG[m]) < winG && rb + j >= keyG[m];
+                vis = (unsigned)(rb + qt * 16 + j - keyG[m]) < winG;
               else
-                vis = keyok[m] && (!kagent[m] || (unsigned)(rb + j - agentG0) < agentGn);
-              P[j] = vis ? P[j] : 0.f;
+                vis = keyok[m] && (!kagent[m] || (unsigned)(rb + qt * 16 + j - agentG0) < agentGn);
+              P[qt][j] = vis ? P[qt][j] : 0.f;
             }
-          }
+        }
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
           f32x4 dS;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) dS[j] = P[j] * dP[j];
-          Ph[m][qt] = pack4(P);
+          for (int j = 0; j < 4; ++j) dS[j] = P[qt][j] * dP[qt][j];
+          Ph[m][qt] = pack4(P[qt]);
           dSh[m][qt] = pack4(dS);
         }
       }
-#pragma unroll
-      for (int m = 0; m < KV_TPW; ++m) {
+      for (int m = 0; m < TPW; ++m) {
         Pb[m] = join8(Ph[m][0], Ph[m][1]);
         dSb[m] = join8(dSh[m][0], dSh[m][1]);
       }
@@ -534,12 +586,14 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       bf16x8 qta[4], dota[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const int o0 = tr_piece_off(0, dt, li, lg), o1 = tr_piece_off(1, dt, li, lg);
-        qta[dt] = join8(ld_lds_tr4(b.Q + o0), ld_lds_tr4(b.Q + o1));
-        dota[dt] = join8(ld_lds_tr4(b.dO + o0), ld_lds_tr4(b.dO + o1));
+        const char* t0 = bb + offT[dt];
+        qta[dt] = join8(ld_lds_tr4(reinterpret_cast<const bf16*>(t0)),
+                        ld_lds_tr4(reinterpret_cast<const bf16*>(t0 + 2048)));
+        dota[dt] = join8(ld_lds_tr4(reinterpret_cast<const bf16*>(t0 + KV_QC * 128)),
+                         ld_lds_tr4(reinterpret_cast<const bf16*>(t0 + KV_QC * 128 + 2048)));
       }
 #pragma unroll
-      for (int m = 0; m < KV_TPW; ++m) {
+      for (int m = 0; m < TPW; ++m) {
         if (!work[m]) continue;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
@@ -552,7 +606,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   }
 
 #pragma unroll
-  for (int m = 0; m < KV_TPW; ++m) {
+  for (int m = 0; m < TPW; ++m) {
     const int key = kb0 + (wave + KV_W * m) * 16 + li;
     if (key >= kend) continue;
     bf16* dkd = p.dk + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
@@ -624,11 +678,21 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   const long g2 = problems * p.kvb;
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 
+  // blocks of up to 256 keys need only two tile slots per wave (fewer
+  // registers); up to 320 take three
+  const bool tpw2 = p.kbl <= KV_W * 2 * 16;
+  const dim3 g2d((unsigned)g2), b2d(KV_W * 64);
   if (d.op == OP_SPACE) {
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<OP_SPACE>, dim3((unsigned)g2), dim3(KV_W * 64), 0, stream, p);
+    if (tpw2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2>), g2d, b2d, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3>), g2d, b2d, 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<OP_TIME>, dim3((unsigned)g2), dim3(KV_W * 64), 0, stream, p);
+    if (tpw2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 2>), g2d, b2d, 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3>), g2d, b2d, 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   }
   return hipGetLastError();

@@ -33,10 +33,10 @@ OPS = [
     (r"attn_fwd_kernel<2>", "time_decode"),
     (r"attn_fwd_kernel<0>", "space_fwd"),
     (r"attn_fwd_kernel<1>", "time_fwd"),
-    (r"attn_bwd_dq_kernel<0>", "space_bwd"),
-    (r"attn_bwd_dkv_kernel<0>", "space_bwd"),
-    (r"attn_bwd_dq_kernel<1>", "time_bwd"),
-    (r"attn_bwd_dkv_kernel<1>", "time_bwd"),
+    (r"attn_bwd_dq_kernel<0[,>]", "space_bwd"),
+    (r"attn_bwd_dkv_kernel<0[,>]", "space_bwd"),
+    (r"attn_bwd_dq_kernel<1[,>]", "time_bwd"),
+    (r"attn_bwd_dkv_kernel<1[,>]", "time_bwd"),
     (r"rmsnorm_rows_kernel", "qkv_proj"),
     (r"gemm256_kernel<0[,>]", "qkv_proj"),
     (r"gemm_nt_kernel<0>", "qkv_proj"),

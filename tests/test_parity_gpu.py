@@ -96,6 +96,9 @@ RAGGED += [
     C.Workload("time_T1024_W192", "time", 1, 1024, 2, 6, 2, 64, "bf16", 192, 0, 0, 1.0, 9013),
     C.Workload("time_T700_W0", "time", 1, 700, 1, 6, 2, 64, "bf16", 0, 0, 0, 1.0, 9014),
     C.Workload("time_T650_W333", "time", 1, 650, 2, 3, 1, 64, "bf16", 333, 0, 0, 1.0, 9015),
+    # one key block of 257..320 keys: three 16-key tiles per dkv wave
+    C.Workload("time_T300_W192", "time", 1, 300, 2, 6, 2, 64, "bf16", 192, 0, 0, 1.0, 9016),
+    C.Workload("time_T272_W0", "time", 1, 272, 1, 4, 1, 64, "bf16", 0, 0, 0, 1.0, 9017),
     # short problems (at most 32 keys and 64 folded rows: one wave per
     # problem), one case per (rows, keys) instance, and the MFMA kernels just
     # past that limit
