@@ -63,8 +63,8 @@ KERNELS = {
     "space_fwd_block": "attn_fwd_kernel<0>",
     "space_fwd": "attn_fwd_kernel<0>",
     "time_fwd": "attn_fwd_kernel<1>",
-    "space_bwd": "attn_bwd_dq_kernel<0> + attn_bwd_dkv_kernel<0, 2|3>",
-    "time_bwd": "attn_bwd_dq_kernel<1> + attn_bwd_dkv_kernel<1, 2|3>",
+    "space_bwd": "attn_bwd_dkv_kernel<0, TPW, FQ> [+ attn_bwd_dq_kernel<0> past 320 keys]",
+    "time_bwd": "attn_bwd_dkv_kernel<1, TPW, FQ> [+ attn_bwd_dq_kernel<1> past 320 keys]",
     "qkv_proj": "rmsnorm_rows_kernel + gemm256_kernel<0, 8>",
     "out_proj": "gemm256_kernel<1, 6>",
 }

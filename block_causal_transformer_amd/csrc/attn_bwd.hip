@@ -25,20 +25,24 @@
 //             one chunk ahead): S = Q K^T and dP = dO V^T, then dV^T += dO^T P
 //             and dK^T += Q^T dS on MFMA, with the Q^T and dO^T operands read
 //             straight from the row-major chunk by transposing LDS reads.
-//             Staging a chunk also forms its rows' Delta from dO and O, which
-//             it leaves in the workspace for the second kernel.
-//  dq kernel  (query-parallel, laid out like the forward): a workgroup holds
-//             K, V and K^T of one (unit, KV head) problem in LDS; each wave
-//             owns 32 query rows (position x head-in-group) and sweeps the
-//             visible keys in 32-key steps: S^T = K Q^T and dP^T = V dO^T on
-//             MFMA (every lane holds one query column), P^T and dS^T on VALU,
-//             dQ^T += K^T dS^T on MFMA.
+//             Staging a chunk also forms its rows' Delta from dO and O.
+//             When the problem's keys fit one block (at most 320: every
+//             dynamics shape), the kernel also forms dQ: each chunk's dS
+//             goes to LDS, and during the next chunk every wave forms one
+//             16 x 16 block of that chunk's dQ^T = K^T dS^T from it and an LDS
+//             copy of K.  The dq kernel is then not launched.
+//  dq kernel  (query-parallel, laid out like the forward; longer problems
+//             only): a workgroup holds K, V and K^T of one (unit, KV head)
+//             problem's key block in LDS; each wave owns 32 query rows
+//             (position x head-in-group) and sweeps the visible keys in
+//             32-key steps: S^T = K Q^T and dP^T = V dO^T on MFMA (every lane
+//             holds one query column), P^T and dS^T on VALU, dQ^T += K^T dS^T
+//             on MFMA.  Delta comes from the workspace the dkv kernel wrote.
 //
-// Key steps (dq) and query chunks (dkv) that the causal / window ranges make
-// invisible are never visited.  The split costs two more matmul passes than a
-// fused kernel (S and dP are formed in both) in exchange for half the
-// register footprint per wave, no LDS exchange of dS, and two (dkv) or three
-// (dq) waves per SIMD.
+// Key steps (dq, and the dQ steps of the dkv kernel) and query chunks (dkv)
+// that the causal / window ranges make invisible are never visited.  For
+// long problems the split costs two more matmul passes (S and dP are formed
+// in both kernels) in exchange for no cross-workgroup sum of dQ.
 #include "bca_device.h"
 #include "bca_kernels.h"
 
@@ -325,6 +329,32 @@ struct KvBuf {
 // the lane offsets below add 16 rows as 2048 bytes and reach dO from Q
 static_assert(offsetof(KvBuf, dO) == KV_QC * 64 * 2, "KvBuf layout");
 
+// With the query gradient formed in the same kernel (FQ), the block's K rows
+// stay in LDS (row-major, zero past the end) and each chunk's dS goes to one
+// of two key-major buffers [key][32 rows], read back transposed as the B
+// operand of dQ^T = K^T dS^T.
+template <bool FQ>
+struct KvSmem {
+  KvBuf sbuf[2];
+};
+template <>
+struct KvSmem<true> {
+  KvBuf sbuf[2];
+  bf16 K[KMAX * 64];
+  bf16 dS[2][KMAX * KV_QC];
+};
+// Both buffers are laid out in 8-byte pieces swizzled so that every 32-lane
+// half of a read or write touches 64 distinct 4-byte banks: K's 16 pieces of
+// 4 head dims per key are xored with 4 * (bit 1 and bit 3 of the key), dS's 8
+// pieces of 4 rows per key with 2 * (bits 2..3 of the key).
+__device__ __forceinline__ int kq_off(int key, int d) {  // [KMAX][64]
+  const int m = ((key >> 1) & 1) | (((key >> 3) & 1) << 1);
+  return key * 64 + (((d >> 2) ^ (m << 2)) << 2) + (d & 3);
+}
+__device__ __forceinline__ int ds_off(int key, int row) {  // [KMAX][32]
+  return key * KV_QC + (((row >> 2) ^ (((key >> 2) & 3) << 1)) << 2) + (row & 3);
+}
+
 // One workgroup per (unit, KV head) problem.  Each wave keeps the K and V
 // rows of its tiles (the B operands of S and dP) and their dK^T, dV^T
 // accumulators in registers for the whole kernel; only the query rows pass
@@ -336,10 +366,11 @@ static_assert(offsetof(KvBuf, dO) == KV_QC * 64 * 2, "KvBuf layout");
 // an agent row iff agent_begin*G <= r < (agent_begin + agent_count)*G.
 // Keys past the end only feed their own (discarded) dK, dV columns here, so
 // they need no mask.
-template <int OP, int TPW>
+template <int OP, int TPW, bool FQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) KvBuf sbuf[2];
+  __shared__ __attribute__((aligned(16))) KvSmem<FQ> sm;
+  KvBuf* sbuf = sm.sbuf;
 
   // workgroup = (problem, block of kbl keys); one block for L <= 320
   int ug, kb;
@@ -360,8 +391,10 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const int nkt = (kend - kb0 + 15) >> 4;
 
   // K and V operands of the wave's tiles, straight from global memory
-  // (keys past the end read as zero)
-  bf16x8 KB[TPW][2], VB[TPW][2];
+  // (keys past the end read as zero); with FQ and three tiles the K operands
+  // are read from the LDS copy of K at each use instead (register pressure)
+  constexpr bool KB_LDS = FQ && TPW >= 3;
+  bf16x8 KB[KB_LDS ? 1 : TPW][2], VB[TPW][2];
   int keyG[TPW];    // time: key * G
   bool kagent[TPW];  // space: the lane's key is an agent key
   bool keyok[TPW];
@@ -374,7 +407,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     for (int s = 0; s < 2; ++s) {
       const bf16x8 kv = ld_global16(p.k + off + (s * 4 + lg) * 8);
       const bf16x8 vv = ld_global16(p.v + off + (s * 4 + lg) * 8);
-      KB[m][s] = ok ? kv : zero8();
+      if constexpr (!KB_LDS) KB[m][s] = ok ? kv : zero8();
       VB[m][s] = ok ? vv : zero8();
     }
     keyG[m] = key * G;
@@ -441,7 +474,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       t += dpp_f32<0x141>(t);
       if (sch == 0) {
         b.delta[srow] = t;
-        if (pre_valid) p.delta[pre_lo] = t;
+        if (!FQ && pre_valid) p.delta[pre_lo] = t;
       }
     }
   };
@@ -471,6 +504,68 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   for (int s = 0; s < 2; ++s) asm volatile("" : "+v"(offQ[s]));
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) asm volatile("" : "+v"(offT[dt]));
+  // FQ: the block's K rows into LDS, rows up to a multiple of 32 keys
+  // (zero past the end, so that dS of those keys meets zero K)
+  const int nks = ((nkt * 16 + 31) >> 5) << 5;  // keys covered by the dQ steps
+  if constexpr (FQ) {
+    const bf16* kbase = p.k + gk.base + g * 64;
+    for (int idx = tid; idx < nks * 8; idx += KV_W * 64) {
+      const int r = idx >> 3, ch = idx & 7;
+      const bool ok = kb0 + r < kend;
+      const bf16x8 kv = ok ? ld_global16(kbase + (int64_t)(kb0 + r) * gk.pos_stride + ch * 8) : zero8();
+      st_lds16(sm.K + kq_off(r, ch * 8), kv);
+    }
+  }
+  // FQ, dQ of chunk cq from its dS buffer: wave w forms the 16 x 16 block of
+  // dQ^T for head-dim slice w & 3 and row half w >> 2, over the 32-key steps
+  // that hold the chunk's visible keys
+  // Lane offsets (elements) into the swizzled K and dS buffers, formed once:
+  // the swizzles depend only on key bits 1..3, so moving by 16 keys (a tile)
+  // or 32 (a dQ step) adds a constant.  dQ reads: key 8 lg + (li >> 2) (+4)
+  // of a step, head dims (w & 3)*16 + 4 (li & 3), rows (w >> 2)*16 + 4 (li & 3);
+  // dS writes: key li of a tile, rows 16 qt + 4 lg; K operand reads (three
+  // slots): key li of a tile, head dims 8 (4 s + lg).
+  int oK[2] = {0, 0}, oD[2] = {0, 0}, oW[2] = {0, 0}, oB[2] = {0, 0};
+  if constexpr (FQ) {
+    const int kq = 8 * lg + (li >> 2);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      oK[e] = kq_off(kq + 4 * e, (wave & 3) * 16 + 4 * (li & 3));
+      oD[e] = ds_off(kq + 4 * e, (wave >> 2) * 16 + 4 * (li & 3));
+      oW[e] = ds_off(li, e * 16 + 4 * lg);
+      oB[e] = kq_off(li, (4 * e + lg) * 8);
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) asm volatile("" : "+v"(oK[e]), "+v"(oD[e]), "+v"(oW[e]), "+v"(oB[e]));
+  }
+  auto dq_phase = [&](int cq) {
+    if constexpr (FQ) {
+      const int r0q = cq * KV_QC;
+      const int qlo = r0q / G, qhi = (min(r0q + KV_QC, p.rows) - 1) / G;
+      int klo, khi;
+      key_range(md, qlo, qhi, klo, khi);
+      const int st0 = max(klo - kb0, 0) >> 5, st1 = (min(khi, kend) - kb0 + 31) >> 5;
+      const int dsl = wave & 3, hq = wave >> 2;
+      const bf16* dsb = sm.dS[cq & 1];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int st = st0; st < st1; ++st) {
+        // four head-dim columns of K and four rows of dS per lane and read
+        const bf16* kst = sm.K + st * 32 * 64;
+        const bf16* dst_ = dsb + st * 32 * KV_QC;
+        const bf16x8 a = join8(ld_lds_tr4(kst + oK[0]), ld_lds_tr4(kst + oK[1]));
+        const bf16x8 bq = join8(ld_lds_tr4(dst_ + oD[0]), ld_lds_tr4(dst_ + oD[1]));
+        acc = mfma16(a, bq, acc);
+      }
+      // lane (li, lg): row hq*16 + li of the chunk, head dims dsl*16 + 4 lg ..
+      const int r = r0q + hq * 16 + li;
+      if (r < p.rows) {
+        const int pos = row_pos(r, p.inv_g);
+        const int hh = r - pos * G;
+        bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + dsl * 16 + lg * 4;
+        *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(acc * p.scale));
+      }
+    }
+  };
   fetch(c_lo);
   stage(sbuf[c_lo & 1]);
   if (c_lo + 1 < nchunks) fetch(c_lo + 1);
@@ -531,11 +626,19 @@ void attn_bwd_dkv_kernel(BwdParams p) {
           load_stats();
         }
         f32x4 S[2], dP[2], P[2];
+        bf16x8 kop[2];
+        if constexpr (KB_LDS) {
+          kop[0] = ld_lds16(sm.K + (wave + KV_W * m) * 16 * 64 + oB[0]);
+          kop[1] = ld_lds16(sm.K + (wave + KV_W * m) * 16 * 64 + oB[1]);
+        } else {
+          kop[0] = KB[m][0];
+          kop[1] = KB[m][1];
+        }
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           S[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          S[qt] = mfma16(Qa[qt][0], KB[m][0], S[qt]);
-          S[qt] = mfma16(Qa[qt][1], KB[m][1], S[qt]);
+          S[qt] = mfma16(Qa[qt][0], kop[0], S[qt]);
+          S[qt] = mfma16(Qa[qt][1], kop[1], S[qt]);
         }
         // the accumulator starts at -Delta, so it ends at dP - Delta
 #pragma unroll
@@ -574,6 +677,26 @@ void attn_bwd_dkv_kernel(BwdParams p) {
         dSb[m] = join8(dSh[m][0], dSh[m][1]);
       }
     }
+    if constexpr (FQ) {
+      // this chunk's dS (zero for tiles that see none of its rows), for the
+      // dQ step of the next iteration; lane (li, lg) holds rows 4 lg .. +3 of
+      // each half for key li of the tile
+      bf16* dsw = sm.dS[c & 1];
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const int t = wave + KV_W * m;
+        if (t * 16 >= nks) continue;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          u32x2 v = {0u, 0u};
+          if (work[m]) {
+            const u32x4 w4 = __builtin_bit_cast(u32x4, dSb[m]);
+            v = qt ? u32x2{w4[2], w4[3]} : u32x2{w4[0], w4[1]};
+          }
+          *reinterpret_cast<u32x2*>(dsw + t * 16 * KV_QC + oW[qt]) = v;
+        }
+      }
+    }
     // the next chunk goes into the other buffer (last read before the
     // previous barrier) while this chunk's second phase runs
     if (c + 1 < nchunks) {
@@ -602,8 +725,12 @@ void attn_bwd_dkv_kernel(BwdParams p) {
         }
       }
     }
+    // the previous chunk's dS buffer is complete (written before the last
+    // barrier) and is rewritten only after the next one
+    if (FQ && c > c_lo) dq_phase(c - 1);
     __syncthreads();
   }
+  if (FQ && nchunks > c_lo) dq_phase(nchunks - 1);
 
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
@@ -681,19 +808,30 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   // blocks of up to 256 keys need only two tile slots per wave (fewer
   // registers); up to 320 take three
   const bool tpw2 = p.kbl <= KV_W * 2 * 16;
+  // one key block per problem: the dkv kernel forms dQ as well (from each
+  // chunk's dS, which it holds in LDS), and the dq kernel is not launched
+  const bool fq = p.kvb == 1;
   const dim3 g2d((unsigned)g2), b2d(KV_W * 64);
   if (d.op == OP_SPACE) {
-    if (tpw2)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2>), g2d, b2d, 0, stream, p);
+    if (fq && tpw2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2, true>), g2d, b2d, 0, stream, p);
+    else if (fq)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, true>), g2d, b2d, 0, stream, p);
+    else if (tpw2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2, false>), g2d, b2d, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3>), g2d, b2d, 0, stream, p);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, false>), g2d, b2d, 0, stream, p);
+    if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   } else {
-    if (tpw2)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 2>), g2d, b2d, 0, stream, p);
+    if (fq && tpw2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 2, true>), g2d, b2d, 0, stream, p);
+    else if (fq)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), g2d, b2d, 0, stream, p);
+    else if (tpw2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 2, false>), g2d, b2d, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3>), g2d, b2d, 0, stream, p);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, false>), g2d, b2d, 0, stream, p);
+    if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   }
   return hipGetLastError();
 }

@@ -155,7 +155,9 @@ int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const voi
 
 /* Bytes of device workspace the backward of `op` needs for `shape`: one fp32
  * Delta = rowsum(dO * O) per (query, head), i.e. B*T*N*Hq*4 bytes.  Returns 0
- * for an invalid shape. */
+ * for an invalid shape.  (The backward only writes it when the attended
+ * sequence, N for space and T for time, is longer than 320; callers pass it
+ * regardless.) */
 size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape);
 
 /* ---- projections beside attention ----
