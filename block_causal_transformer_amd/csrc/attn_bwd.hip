@@ -323,8 +323,8 @@ __device__ __forceinline__ float dpp_f32(float x) {
 struct KvBuf {
   bf16 Q[KV_QC * 64];
   bf16 dO[KV_QC * 64];
-  float lse[KV_QC];
-  float delta[KV_QC];
+  float lse[KV_QC];     // log2-scaled LSE of the rows (+inf for padding)
+  float ndelta[KV_QC];  // -Delta of the rows
 };
 // the lane offsets below add 16 rows as 2048 bytes and reach dO from Q
 static_assert(offsetof(KvBuf, dO) == KV_QC * 64 * 2, "KvBuf layout");
@@ -473,7 +473,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       t += dpp_f32<0x4E>(t);
       t += dpp_f32<0x141>(t);
       if (sch == 0) {
-        b.delta[srow] = t;
+        b.ndelta[srow] = -t;
         if (!FQ && pre_valid) p.delta[pre_lo] = t;
       }
     }
@@ -603,7 +603,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
-          ndl4[qt] = -*reinterpret_cast<const f32x4*>(b.delta + qt * 16 + lg * 4);
+          ndl4[qt] = *reinterpret_cast<const f32x4*>(b.ndelta + qt * 16 + lg * 4);
         }
       };
 #pragma unroll
