@@ -1,7 +1,7 @@
 """Turn rocprofv3 CSV output into the short text summaries kept in profiles/.
 
     python -m block_causal_transformer_amd.rocprof_summary stats \\
-        KERNEL_STATS_CSV OUT_MD --cmd "the profiled command"
+        KERNEL_STATS_CSV OUT_MD --cmd "the profiled command" [--bench-log LOG]
     python -m block_causal_transformer_amd.rocprof_summary traffic \\
         FETCH_COUNTER_CSV WRITE_COUNTER_CSV OUT_TXT --cmd "..." --sources a.hip,b.h
 
@@ -20,6 +20,7 @@ import argparse
 import collections
 import csv
 import hashlib
+import json
 import os
 import re
 import sys
@@ -94,6 +95,17 @@ def cmd_stats(args):
     for op in OP_ORDER:
         if op in per_op:
             out.append("| %s | %.1f |" % (op, per_op[op]))
+    if args.bench_log:
+        # the bench's own HIP-event timing of each op in the same profiled run
+        line = next((l for l in open(args.bench_log) if l.startswith("{")), None)
+        if line:
+            d = json.loads(line)
+            out += ["", "`bench.py`'s HIP-event average per op in the same (profiled) run, "
+                    "ms_per_step %.4f:" % d["ms_per_step"], "",
+                    "| op | events (us) | kernel trace (us) |", "|---|---|---|"]
+            for op, v in d.get("ops", {}).items():
+                kt = per_op.get({"space_fwd_block": "space_fwd"}.get(op, op))
+                out.append("| %s | %.1f | %s |" % (op, 1e3 * v["ms"], "%.1f" % kt if kt else "-"))
     out.append("")
     with open(args.out, "w") as f:
         f.write("\n".join(out))
@@ -164,6 +176,9 @@ def main(argv=None):
     a.add_argument("csv")
     a.add_argument("out")
     a.add_argument("--cmd", required=True)
+    a.add_argument("--bench-log", default=None,
+                   help="stdout of the profiled bench.py run: its JSON line's per-op event "
+                        "timings are listed beside the kernel trace")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
