@@ -89,6 +89,7 @@ void attn_fwd_kernel(FwdParams p) {
   const UnitGeom gk = unit_geom(MOP, u, p.Tk, p.N, p.Hkv, 64);
   const UnitGeom gl = unit_geom(MOP, u, p.T, p.N, p.Hq, 1);
   const MaskDesc md{MOP, p.L, p.window, p.agent_begin, p.agent_count};
+  const unsigned weff = (unsigned)(p.window > 0 ? p.window : p.L);
   auto kframe = [&](int x) { return OP == OP_DECODE ? (p.kfirst + x) % p.Tk : x; };
   const bf16* kbase = p.k + gk.base + g * 64;
   const bf16* vbase = p.v + gk.base + g * 64;
@@ -209,15 +210,25 @@ void attn_fwd_kernel(FwdParams p) {
           // a select, not a conditional store: hipcc dropped conditional
           // element stores into this array of vectors
 #pragma unroll
-          for (int qt = 0; qt < NQT; ++qt)
+          for (int qt = 0; qt < NQT; ++qt) {
+            // time: the query sits at a real position (< L), so a key is
+            // visible iff 0 <= query - key < window (the whole sequence when
+            // there is none): one unsigned compare, and keys past the end
+            // fail it too
+            const int dq0 = qpos[qt] + qsh - kabs - lg * 4;
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const bool vis = visible_op<MOP>(md, qpos[qt] + qsh, kabs + h * 16 + lg * 4 + j);
+                bool vis;
+                if constexpr (MOP == OP_TIME)
+                  vis = (unsigned)(dq0 - h * 16 - j) < weff;
+                else
+                  vis = visible_op<MOP>(md, qpos[qt] + qsh, kabs + h * 16 + lg * 4 + j);
                 const float cur = sc[qt][h][j];
                 sc[qt][h][j] = vis ? cur : -INFINITY;
               }
+          }
         }
         // online softmax with a lazy reference max (log2 domain): a row's
         // reference moves only when one of its scores exceeds it by more
