@@ -18,7 +18,7 @@ visible (query, key, head) pair forward and 10*D backward; masked and padded
 work is never counted.  Per-op kernel durations come from HIP events on the
 stream the kernels run on.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--no-cpu-baseline]
 
 ``--workload rollout_decode`` instead times one step of frame-by-frame
 generation (section "Artefacts publiés": rollout generation, the demo
@@ -448,8 +448,11 @@ def main_proj(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200, enough to time the GPU at its steady clock)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 100; the clock ramps up over the first "
+                         "few tens of milliseconds of work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
@@ -463,9 +466,11 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the op shards by block / slot with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+    if args.steps is None:
+        args.steps = 200
+    if args.warmup is None:
+        args.warmup = 100
     if args.workload == "rollout_decode":
-        if args.steps == 30 and args.warmup == 5:
-            args.steps, args.warmup = 200, 20
         return main_decode(args)
     if args.workload == "projections":
         return main_proj(args)

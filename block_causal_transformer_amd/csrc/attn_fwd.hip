@@ -138,6 +138,10 @@ void attn_fwd_kernel(FwdParams p) {
     bool qvalid[NQT];
     f32x4 acc[NQT][4];
     float m[NQT], l[NQT];
+    // per row, kept in step with m: -m (0 while m = -inf) for the exp
+    // argument, and the raw-score threshold (m + 2^8 in log2 units, divided
+    // by the scale) above which the row may need a new reference
+    float negm[NQT], thr[NQT];
     int qlo = 0, qhi = 0;
     if (active) {
 #pragma unroll
@@ -150,6 +154,8 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) acc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[qt] = -INFINITY;
+        negm[qt] = 0.f;
+        thr[qt] = -INFINITY;
         l[qt] = 0.f;
       }
       qlo = r0 / G + qsh;
@@ -236,19 +242,20 @@ void attn_fwd_kernel(FwdParams p) {
         // exactly 1), so every row depends on its own scores alone
         // each lane first tests its own 8 scores of the row; the 4-lane
         // row maximum is formed only when some lane of the wave is over
-        float lmx[NQT];
+        float lmx[NQT];  // raw (unscaled) maximum of the lane's 8 scores of the row
         bool over = false;
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
           const float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
           const float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
-          lmx[qt] = fmaxf(a, b) * p.scale_log2;
-          over |= lmx[qt] > m[qt] + kRescaleThreshold;
+          lmx[qt] = fmaxf(a, b);
+          over |= lmx[qt] > thr[qt];
         }
         if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
           for (int qt = 0; qt < NQT; ++qt) {
-            const float mx = group4_max(lmx[qt]);
+            // the scale is positive, so scaling commutes with the maximum
+            const float mx = group4_max(lmx[qt]) * p.scale_log2;
             const bool grow = mx > m[qt] + kRescaleThreshold;
             const float mn = grow ? mx : m[qt];
             const float alpha = grow ? fast_exp2(m[qt] - mn) : 1.f;
@@ -256,17 +263,18 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) acc[qt][dt] *= alpha;
             m[qt] = mn;
+            negm[qt] = (mn == -INFINITY) ? 0.f : -mn;
+            thr[qt] = (mn + kRescaleThreshold) / p.scale_log2;
           }
         }
         bf16x8 pb[NQT];
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
-          const float mref = (m[qt] == -INFINITY) ? 0.f : m[qt];
           f32x4 e0, e1;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            e0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, -mref));
-            e1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, -mref));
+            e0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, negm[qt]));
+            e1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, negm[qt]));
           }
           l[qt] += ((e0[0] + e0[1]) + (e0[2] + e0[3])) + ((e1[0] + e1[1]) + (e1[2] + e1[3]));
           pb[qt] = pack8(e0, e1);
