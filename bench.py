@@ -136,6 +136,14 @@ def cpu_baseline(target_s: float = 15.0):
     }
 
 
+def spread(samples):
+    """Median, 10th and 90th percentile (ms) of per-step event durations."""
+    import numpy as np
+    a = np.asarray(samples, dtype=np.float64)
+    return {"ms_median": round(float(np.median(a)), 5), "ms_p10": round(float(np.percentile(a, 10)), 5),
+            "ms_p90": round(float(np.percentile(a, 90)), 5)}
+
+
 def roofline_of(flop, min_bytes, ms):
     intensity = flop / min_bytes
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)
@@ -402,10 +410,11 @@ def main_proj(args):
     total = 0.0
     for i, (name, _) in enumerate(seq):
         which = "qkv" if name == "qkv_proj" else "out"
-        ms = sum(evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)) / args.steps
+        samples = [evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]
+        ms = sum(samples) / args.steps
         fl, by = C.proj_flops(w, which), C.proj_min_bytes(w, which)
         total += fl
-        ops_[name] = {"ms": round(ms, 5), "tflops": round(fl / ms / 1e9, 2),
+        ops_[name] = {"ms": round(ms, 5), **spread(samples), "tflops": round(fl / ms / 1e9, 2),
                       "pct_mfma_peak": round(100.0 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
                       "gbps": round(by / ms / 1e6, 1), "flop": fl, "min_bytes": by}
     # the roofline is quoted on the output projection's GEMM: one launch per
@@ -488,10 +497,10 @@ def step_workloads(name):
                 "frames x 290 slots, causal, window 192)",
                 "block-causal attention TFLOP/s (fwd, fwd+bwd) and % of MI355X bf16 MFMA peak")
     if name == "tokenizer_step":
-        return ([C.get("5a"), C.get("5b"), C.get("5c")],
+        return ([C.get("5a"), C.get("5d"), C.get("5b"), C.get("5c")],
                 "Tokenizer attention step: encoder space layer (16 frames of 1432 tokens, 24 heads "
-                "MHA, dense) + decoder space layer (16 heads) + decoder time layer (1432 slots x 16 "
-                "frames, causal, window 16), each fwd+bwd",
+                "MHA, dense) + encoder time layer (1432 slots x 16 frames, 24 heads, causal, window "
+                "16) + decoder space layer (16 heads) + decoder time layer (16 heads), each fwd+bwd",
                 "tokenizer attention TFLOP/s (fwd+bwd) and % of MI355X bf16 MFMA peak")
     if name == "long_time":
         return ([C.get("4").with_(name="4L", T=1024, seed=4100)],
@@ -583,12 +592,14 @@ def main_step(args):
     total_flops = 0.0
     for i, key in enumerate(seq):
         w = bufs[key[0]]["w"]
-        ms = sum(evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)) / args.steps
+        samples = [evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps)]
+        ms = sum(samples) / args.steps
         fl = C.flops(w, key[1])
         by = C.min_bytes(w, key[1])
         total_flops += fl
         per_op[labels[key]] = {
             "ms": round(ms, 5),
+            **spread(samples),
             "tflops": round(fl / ms / 1e9, 2),
             "pct_mfma_peak": round(100.0 * fl / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
             "gbps": round(by / ms / 1e6, 1),

@@ -144,6 +144,8 @@ def _mk() -> Dict[str, Workload]:
                        note="tokenizer decoder space layer")
     c["5c"] = Workload("5c", TIME, 1, 16, 1432, 16, 16, 64, "bf16", 16, 0, 0, 1.0, 5002,
                        note="tokenizer decoder time layer, window 16")
+    c["5d"] = Workload("5d", TIME, 1, 16, 1432, 24, 24, 64, "bf16", 16, 0, 0, 1.0, 5003,
+                       note="tokenizer encoder time layer (24 heads, MHA), window 16")
     return c
 
 

@@ -38,11 +38,11 @@ def _run(w, x, bwd=True):
     return {n: t.detach().cpu() for n, t in out.items()}
 
 
-@pytest.mark.parametrize("name", ["3", "4", "5c"])
+@pytest.mark.parametrize("name", ["3", "4", "5c", "5d"])
 def test_bitwise_determinism(name):
     _needs_gpu()
     w = {"3": C.get("3").with_(B=1, T=3), "4": C.get("4").with_(N=3),
-         "5c": C.get("5c").with_(N=2)}[name]
+         "5c": C.get("5c").with_(N=2), "5d": C.get("5d").with_(N=2)}[name]
     x = gen.make_inputs(w)
     a, b = _run(w, x), _run(w, x)
     for n in a:

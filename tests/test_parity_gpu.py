@@ -36,6 +36,7 @@ REDUCED = {
     "5a": C.get("5a").with_(T=1),
     "5b": C.get("5b").with_(T=1, Hq=4, Hkv=4),
     "5c": C.get("5c").with_(N=5),
+    "5d": C.get("5d").with_(N=3),
 }
 
 
@@ -58,6 +59,7 @@ FULL_SAMPLES = {
     "5a": [0, 15],
     "5b": [7],
     "5c": [0, 700, 1431],
+    "5d": [3, 1000],
 }
 
 
