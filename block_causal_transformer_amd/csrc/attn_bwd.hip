@@ -456,9 +456,9 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     pre_lo = lo;
   };
   // Delta = rowsum(dO * O) is formed here, from the 8 pieces of a row held by
-  // 8 adjacent threads, and written to the workspace for the dq kernel (which
-  // runs after this one); workgroups whose chunk ranges overlap write the
-  // same bits
+  // 8 adjacent threads; the chunk buffer keeps -Delta, and without FQ it also
+  // goes to the workspace for the dq kernel (which runs after this one), where
+  // workgroups whose chunk ranges overlap write the same bits
   auto stage = [&](KvBuf& b) {
     st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
     if (carries_q) {

@@ -44,9 +44,10 @@ inline int time_wg_key_span(int L, int G, int W, long rows_per_wg) {
   return span;
 }
 
-// Keys per LDS block of the MFMA backward: the dq kernel streams longer
-// problems through LDS in blocks of this many keys, and the dkv kernel gives
-// every such block its own workgroup.
+// Keys per LDS block of the MFMA backward: the dkv kernel gives every such
+// block its own workgroup (and forms dQ itself when a problem has only one),
+// and the dq kernel streams longer problems through LDS in blocks of this
+// many keys.
 constexpr int kBwdKeyBlock = 320;
 
 // MFMA kernels: bf16, D = 64.
