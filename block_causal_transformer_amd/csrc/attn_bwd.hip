@@ -355,17 +355,17 @@ __device__ __forceinline__ int ds_off(int key, int row) {  // [KMAX][32]
   return key * KV_QC + (((row >> 2) ^ (((key >> 2) & 3) << 1)) << 2) + (row & 3);
 }
 
-// One workgroup per (unit, KV head) problem.  Each wave keeps the K and V
-// rows of its tiles (the B operands of S and dP) and their dK^T, dV^T
-// accumulators in registers for the whole kernel; only the query rows pass
-// through LDS.  The two waves of a SIMD (w and w + 4) hold 5 of the 20 tile
-// slots between them.
+// One workgroup per (unit, KV head) problem and key block.  Each wave keeps
+// the K and V rows of its tiles (the B operands of S and dP) and their dK^T,
+// dV^T accumulators in registers for the whole kernel; only the query rows
+// pass through LDS.  With three slots the two waves of a SIMD (w and w + 4)
+// hold 5 of the 20 tile slots between them.
 //
 // Masks are tested on folded row indices r = position * G + head: a key k is
 // visible to row r in time attention iff k*G <= r < (k + W)*G, and a row is
 // an agent row iff agent_begin*G <= r < (agent_begin + agent_count)*G.
-// Keys past the end only feed their own (discarded) dK, dV columns here, so
-// they need no mask.
+// Keys past the end need no mask: they only feed their own (discarded) dK, dV
+// columns and, with FQ, dQ through K rows that are zero in LDS.
 template <int OP, int TPW, bool FQ>
 __global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkv_kernel(BwdParams p) {
