@@ -39,7 +39,6 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -54,7 +53,6 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 TRAFFIC_FILE_DECODE = os.path.join(ROOT, "profiles", "hbm_traffic_rollout_decode.txt")
 TRAFFIC_FILE_PROJ = os.path.join(ROOT, "profiles", "hbm_traffic_projections.txt")
-CSRC = os.path.join(ROOT, "block_causal_transformer_amd", "csrc")
 
 
 # kernel launches of each attention call (template argument 0 = space, 1 = time)
@@ -71,16 +69,10 @@ KERNELS = {
 
 
 def source_digest(files=None) -> str:
-    """Digest of the kernel sources ``files`` (names in csrc/; all by default)."""
-    h = hashlib.sha256()
-    for name in sorted(files or os.listdir(CSRC)):
-        path = os.path.join(CSRC, name)
-        if not os.path.exists(path):
-            return ""
-        with open(path, "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Digest of the kernel sources ``files`` (names in csrc/; all by default),
+    comments and layout ignored: the one the counter summaries carry."""
+    from block_causal_transformer_amd.rocprof_summary import source_digest as digest
+    return digest(files)
 
 
 def read_traffic(kernel_key: str, path: str = TRAFFIC_FILE):

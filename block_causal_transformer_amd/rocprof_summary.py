@@ -47,13 +47,43 @@ OPS = [
 OP_ORDER = ("space_fwd", "space_bwd", "time_fwd", "time_bwd", "time_decode", "qkv_proj", "out_proj")
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that editing a comment does not change the digest (string and character
+    literals are kept as they are)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(files=None) -> str:
-    """Digest of the kernel sources ``files`` (names in csrc/; all by default)."""
+    """Digest of the kernel sources ``files`` (names in csrc/; all by default),
+    comments and layout ignored."""
     h = hashlib.sha256()
     for name in sorted(files or os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
+        path = os.path.join(CSRC, name)
+        if not os.path.exists(path):
+            return ""
+        with open(path, encoding="utf-8") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -45,3 +45,17 @@ def test_traffic_summary_is_used_only_for_the_sources_it_was_taken_on(tmp_path):
     gone = tmp_path / "gone.txt"
     gone.write_text("source_files=no_such.hip\nsource_sha=%s\nout_proj.bytes=1\n" % bench.source_digest(files))
     assert bench.read_traffic("out_proj", str(gone)) is None
+
+
+def test_source_digest_ignores_comments(tmp_path, monkeypatch):
+    # the counter summaries stay valid across comment edits, not code edits
+    from block_causal_transformer_amd import rocprof_summary as R
+    src = 'int f(int x) { return x / 2; } // half\n/* note */ const char* s = "//";\n'
+    assert R.strip_comments(src) == 'int f(int x) { return x / 2; } const char* s = "//";'
+    monkeypatch.setattr(R, "CSRC", str(tmp_path))
+    (tmp_path / "k.hip").write_text(src)
+    d0 = R.source_digest(["k.hip"])
+    (tmp_path / "k.hip").write_text(src.replace("// half", "// one half").replace("note", "other"))
+    assert R.source_digest(["k.hip"]) == d0
+    (tmp_path / "k.hip").write_text(src.replace("x / 2", "x / 3"))
+    assert R.source_digest(["k.hip"]) != d0
