@@ -59,3 +59,23 @@ def test_source_digest_ignores_comments(tmp_path, monkeypatch):
     assert R.source_digest(["k.hip"]) == d0
     (tmp_path / "k.hip").write_text(src.replace("x / 2", "x / 3"))
     assert R.source_digest(["k.hip"]) != d0
+
+
+def test_spread_of_step_times():
+    s = bench.spread([1.0] * 8 + [2.0, 9.0])
+    assert s["ms_median"] == 1.0 and s["ms_p10"] == 1.0 and s["ms_p90"] == pytest.approx(2.7)
+
+
+def test_profile_summary_maps_kernel_instances_to_ops():
+    from block_causal_transformer_amd import rocprof_summary as R
+    cases = {
+        "void bca::(anonymous namespace)::attn_bwd_dkv_kernel<0, 3, true>(bca::(anonymous namespace)::BwdParams)": "space_bwd",
+        "void bca::(anonymous namespace)::attn_bwd_dkv_kernel<1, 2, false>(bca::(anonymous namespace)::BwdParams)": "time_bwd",
+        "void bca::(anonymous namespace)::attn_bwd_dq_kernel<1>(bca::(anonymous namespace)::BwdParams)": "time_bwd",
+        "void bca::(anonymous namespace)::attn_fwd_kernel<2>(bca::(anonymous namespace)::FwdParams)": "time_decode",
+        "void bca::(anonymous namespace)::gemm256_kernel<1, 6>(bca::(anonymous namespace)::GemmParams)": "out_proj",
+        "void bca::(anonymous namespace)::gemm256_kernel<0, 8>(bca::(anonymous namespace)::GemmParams)": "qkv_proj",
+        "void at::native::vectorized_elementwise_kernel<4, float>(int)": None,
+    }
+    for name, op in cases.items():
+        assert R.op_of(name) == op, name
