@@ -81,7 +81,16 @@ void attn_fwd_kernel(FwdParams p) {
   constexpr int NT = FW * 64;
 
   int ug, split;
-  xcd_remap(blockIdx.x, p.units * p.Hkv, p.splits, ug, split);
+  if constexpr (OP == OP_TIME) {
+    // causal rows: later row splits see more keys, so they are dispatched
+    // first and the lighter early splits fill the grid's last round
+    const int P = p.units * p.Hkv;
+    const int sidx = blockIdx.x / P;
+    split = p.splits - 1 - sidx;
+    ug = blockIdx.x - sidx * P;
+  } else {
+    xcd_remap(blockIdx.x, p.units * p.Hkv, p.splits, ug, split);
+  }
   const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
   constexpr int MOP = OP == OP_DECODE ? OP_TIME : OP;  // mask and layout kind
   const int qsh = OP == OP_DECODE ? p.qoff : 0;        // query -> key position
