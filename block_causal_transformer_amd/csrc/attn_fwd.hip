@@ -72,10 +72,16 @@ __device__ __forceinline__ int vt_off(int d, int pos) {  // sVT: [64][KMAX]
 // 8 waves of 32 query rows; two workgroups (80 KB of LDS each) share a CU,
 // so each SIMD interleaves four waves.  OP_DECODE runs the time op's code
 // with the query positions shifted by qoff and the key frames read from a
-// ring (rollout over a KV cache).
+// ring (rollout over a KV cache); its chunks are 16 rows (a problem has G
+// rows per new frame), and it keeps V row-major in LDS, reading the PV
+// operand with transposing reads, since its staging, not its few steps,
+// dominates.
 template <int OP>
 __global__ __attribute__((amdgpu_flat_work_group_size(FW * 64, FW * 64), amdgpu_waves_per_eu(4, 4)))
 void attn_fwd_kernel(FwdParams p) {
+  // rows per chunk: a decode problem has only G rows per new frame
+  constexpr int NQ = OP == OP_DECODE ? 1 : NQT;
+  constexpr int QC = 16 * NQ;
   __shared__ __attribute__((aligned(16))) bf16 sK[KMAX * 64];
   __shared__ __attribute__((aligned(16))) bf16 sVT[64 * KMAX];
   constexpr int NT = FW * 64;
@@ -111,7 +117,7 @@ void attn_fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
-  const int nch = (row1 - row0 + QCH - 1) / QCH;
+  const int nch = (row1 - row0 + QC - 1) / QC;
   const int passes = (nch + FW - 1) / FW;
   const int G = p.G;
   // keys [wklo, wkhi) are all that any row of this workgroup sees (32-key
@@ -125,11 +131,11 @@ void attn_fwd_kernel(FwdParams p) {
   // columns read a real (clamped) row and are never stored.  The next
   // chunk's Q is loaded before this chunk's O is stored, so that the first
   // products of the next chunk do not wait behind the stores.
-  bf16x8 qreg[NQT][2];
+  bf16x8 qreg[NQ][2];
   auto load_q = [&](int pass) {
-    const int r0n = row0 + (pass * FW + wave) * QCH;
+    const int r0n = row0 + (pass * FW + wave) * QC;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
+    for (int qt = 0; qt < NQ; ++qt) {
       const int rr = min(r0n + qt * 16 + li, row1 - 1);
       const int pos = row_pos(rr, p.inv_g);
       const bf16* src = qbase + pos * gq.pos_stride + (rr - pos * G) * 64 + lg * 8;
@@ -141,20 +147,20 @@ void attn_fwd_kernel(FwdParams p) {
   for (int pass = 0; pass < passes; ++pass) {
     const int ch = pass * FW + wave;
     const bool active = ch < nch;
-    const int r0 = row0 + ch * QCH;
+    const int r0 = row0 + ch * QC;
 
-    int qpos[NQT], hh[NQT];
-    bool qvalid[NQT];
-    f32x4 acc[NQT][4];
-    float m[NQT], l[NQT];
+    int qpos[NQ], hh[NQ];
+    bool qvalid[NQ];
+    f32x4 acc[NQ][4];
+    float m[NQ], l[NQ];
     // per row, kept in step with m: -m (0 while m = -inf) for the exp
     // argument, and the raw-score threshold (m + 2^8 in log2 units, divided
     // by the scale) above which the row may need a new reference
-    float negm[NQT], thr[NQT];
+    float negm[NQ], thr[NQ];
     int qlo = 0, qhi = 0;
     if (active) {
 #pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
+      for (int qt = 0; qt < NQ; ++qt) {
         const int r = r0 + qt * 16 + li;
         qvalid[qt] = r < row1;
         const int rr = min(r, row1 - 1);
@@ -168,7 +174,7 @@ void attn_fwd_kernel(FwdParams p) {
         l[qt] = 0.f;
       }
       qlo = r0 / G + qsh;
-      qhi = (min(r0 + QCH, row1) - 1) / G + qsh;
+      qhi = (min(r0 + QC, row1) - 1) / G + qsh;
     }
 
     for (int kb = 0; kb < nkb; ++kb) {
@@ -185,9 +191,15 @@ void attn_fwd_kernel(FwdParams p) {
             vv = ld_global16(vbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
           }
           st_lds16(sK + k_off(r, c), kv);
-          const int pp = vt_perm(r);
+          if constexpr (OP == OP_DECODE) {
+            // decode: V stays row-major (laid out as K) and is read back
+            // transposed; one 16-byte write instead of eight 2-byte ones
+            st_lds16(sVT + k_off(r, c), vv);
+          } else {
+            const int pp = vt_perm(r);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sVT[vt_off(c * 8 + e, pp)] = vv[e];
+            for (int e = 0; e < 8; ++e) sVT[vt_off(c * 8 + e, pp)] = vv[e];
+          }
         }
         __syncthreads();
       }
@@ -202,14 +214,14 @@ void attn_fwd_kernel(FwdParams p) {
       for (int st = st0; st < st1; ++st) {
         const int kabs = key0 + st * 32;
         // S^T tiles: rows = 16 keys (two halves of the step), columns = queries
-        f32x4 sc[NQT][2];
+        f32x4 sc[NQ][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int kr = st * 32 + h * 16 + li;
           const bf16x8 k0 = ld_lds16(sK + k_off(kr, lg));
           const bf16x8 k1 = ld_lds16(sK + k_off(kr, 4 + lg));
 #pragma unroll
-          for (int qt = 0; qt < NQT; ++qt) {
+          for (int qt = 0; qt < NQ; ++qt) {
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             z = mfma16(k0, qreg[qt][0], z);
             sc[qt][h] = mfma16(k1, qreg[qt][1], z);
@@ -225,7 +237,7 @@ void attn_fwd_kernel(FwdParams p) {
           // a select, not a conditional store: hipcc dropped conditional
           // element stores into this array of vectors
 #pragma unroll
-          for (int qt = 0; qt < NQT; ++qt) {
+          for (int qt = 0; qt < NQ; ++qt) {
             // time: the query sits at a real position (< L), so a key is
             // visible iff 0 <= query - key < window (the whole sequence when
             // there is none): one unsigned compare, and keys past the end
@@ -251,10 +263,10 @@ void attn_fwd_kernel(FwdParams p) {
         // exactly 1), so every row depends on its own scores alone
         // each lane first tests its own 8 scores of the row; the 4-lane
         // row maximum is formed only when some lane of the wave is over
-        float lmx[NQT];  // raw (unscaled) maximum of the lane's 8 scores of the row
+        float lmx[NQ];  // raw (unscaled) maximum of the lane's 8 scores of the row
         bool over = false;
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
+        for (int qt = 0; qt < NQ; ++qt) {
           const float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
           const float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
           lmx[qt] = fmaxf(a, b);
@@ -262,7 +274,7 @@ void attn_fwd_kernel(FwdParams p) {
         }
         if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
-          for (int qt = 0; qt < NQT; ++qt) {
+          for (int qt = 0; qt < NQ; ++qt) {
             // the scale is positive, so scaling commutes with the maximum
             const float mx = group4_max(lmx[qt]) * p.scale_log2;
             const bool grow = mx > m[qt] + kRescaleThreshold;
@@ -276,9 +288,9 @@ void attn_fwd_kernel(FwdParams p) {
             thr[qt] = (mn + kRescaleThreshold) / p.scale_log2;
           }
         }
-        bf16x8 pb[NQT];
+        bf16x8 pb[NQ];
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
+        for (int qt = 0; qt < NQ; ++qt) {
           f32x4 e0, e1;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -291,9 +303,18 @@ void attn_fwd_kernel(FwdParams p) {
         // O^T += V^T P^T
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 vt = ld_lds16(sVT + vt_off(dt * 16 + li, st * 32 + lg * 8));
+          bf16x8 vt;
+          if constexpr (OP == OP_DECODE) {
+            // lane (li, lg) receives head dim dt*16 + li of keys 4 lg .. +3 and
+            // 16 + 4 lg .. +3 of the step, the keys its P^T operand holds
+            const int kr = st * 32 + 4 * lg + (li >> 2), dcol = dt * 16 + 4 * (li & 3);
+            vt = join8(ld_lds_tr4(sVT + k_off(kr, dcol >> 3) + (dcol & 7)),
+                       ld_lds_tr4(sVT + k_off(kr + 16, dcol >> 3) + (dcol & 7)));
+          } else {
+            vt = ld_lds16(sVT + vt_off(dt * 16 + li, st * 32 + lg * 8));
+          }
 #pragma unroll
-          for (int qt = 0; qt < NQT; ++qt) acc[qt][dt] = mfma16(vt, pb[qt], acc[qt][dt]);
+          for (int qt = 0; qt < NQ; ++qt) acc[qt][dt] = mfma16(vt, pb[qt], acc[qt][dt]);
         }
       }
     }
@@ -301,7 +322,7 @@ void attn_fwd_kernel(FwdParams p) {
     if (active) {
       if (ch + FW < nch) load_q(pass + 1);
 #pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
+      for (int qt = 0; qt < NQ; ++qt) {
         const float lt = group4_sum(l[qt]);
         if (!qvalid[qt]) continue;
         const float inv = 1.f / lt;
@@ -356,7 +377,8 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   // Split each problem's rows over several workgroups so that the grid
   // covers the 256 CUs (two workgroups each) about three times over.
   const long problems = (long)p.units * p.Hkv;
-  const int chunks = (p.rows + QCH - 1) / QCH;
+  const int qch = d.op == OP_DECODE ? 16 : QCH;  // rows per chunk (as in the kernel)
+  const int chunks = (p.rows + qch - 1) / qch;
   int splits = (int)((3 * 512 + problems - 1) / problems);
   splits = max(1, min(splits, (chunks + FW - 1) / FW));
   int per = (chunks + splits - 1) / splits;
@@ -365,8 +387,8 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   // that the keys a workgroup sees fit one LDS block (otherwise every pass
   // restages all its blocks).
   if (d.op == OP_TIME && p.window > 0)
-    while (per > FW && time_wg_key_span(p.L, p.G, p.window, (long)per * QCH) > KMAX) per -= FW;
-  p.rows_per_split = per * QCH;
+    while (per > FW && time_wg_key_span(p.L, p.G, p.window, (long)per * qch) > KMAX) per -= FW;
+  p.rows_per_split = per * qch;
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
   const long grid = problems * p.splits;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidValue;
