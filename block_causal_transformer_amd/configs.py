@@ -47,6 +47,7 @@ class Workload:
     seed: int = 0           # SeedSequence entropy
     shared_rows: Optional[Tuple[int, int]] = None  # (slot_begin, count): MAE mask-token rows
     note: str = ""
+    dout_scale: float = 1.0  # multiply the dO draws before rounding
 
     @property
     def G(self) -> int:

@@ -9,7 +9,8 @@ Recipe (one workload = one ``configs.Workload``):
 * ``SeedSequence(w.seed + variant)`` is spawned into five child streams, in
   order: q, k, v, dO, and an auxiliary stream for structure choices.
 * Each of q, k, v, dO is ``standard_normal(float32)`` of its full shape,
-  multiplied by ``w.value_scale`` (CoinRun inputs are scaled by 1/sqrt(64)),
+  multiplied by ``w.value_scale`` (CoinRun inputs are scaled by 1/sqrt(64);
+  dO by ``w.dout_scale``, 1 unless a test keeps its gradients small),
   then rounded to bf16 with round-to-nearest-even when the workload is bf16.
   fp32 workloads keep the fp32 draws.
 * Tokenizer encoder workloads (``w.shared_rows``): in every frame a seeded
@@ -85,7 +86,7 @@ def make_inputs(w: Workload, variant: int = 0, with_dout: bool = True) -> Dict[s
                 k[b, t, slots] = shared_k
                 v[b, t, slots] = shared_v
     if with_dout:
-        out["dout"] = _draw(rd, w.q_shape(), 1.0, w.dtype)
+        out["dout"] = _draw(rd, w.q_shape(), w.dout_scale, w.dtype)
     return out
 
 

@@ -2,7 +2,8 @@
 the fp64 oracle, through the C ABI: the Minecraft rollout shape in steady
 state (wrapped ring) and at its first frames, several new frames at once, a
 cache larger than the window, an unbounded window longer than one LDS key
-block, head_dim 32 and fp32 (the generic kernel), and decode of frame t
+block, 40 query heads per KV head (several row chunks per new frame),
+head_dim 32 and fp32 (the generic kernel), and decode of frame t
 against row t of the full-sequence time attention kernel."""
 import types
 
@@ -29,6 +30,7 @@ CASES = {
     "batch2_mha": BASE.with_(B=2, Hq=4, Hkv=4, N=9, window=16, cache_frames=20, q_frame0=50, seed=6106),
     "d32": BASE.with_(D=32, N=11, Hq=8, Hkv=2, window=8, cache_frames=8, q_frame0=20, seed=6107),
     "fp32": BASE.with_(dtype="f32", N=6, Hq=4, Hkv=2, D=32, window=4, cache_frames=5, q_frame0=9, seed=6108),
+    "g40": BASE.with_(Hq=40, Hkv=1, N=3, window=8, cache_frames=8, q_frame0=20, seed=6109),
 }
 
 
