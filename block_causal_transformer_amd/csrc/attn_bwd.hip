@@ -297,8 +297,11 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
 // ------------------------------------------------------------ dkv kernel
 
-constexpr int KV_W = 8;    // waves per workgroup
-constexpr int KV_TPW = 3;  // most 16-key tile slots per wave (tile = wave + 8 * slot)
+// Key blocks of up to 256 keys: 16 waves of one 16-key tile each (four waves
+// per SIMD); up to 320: 8 waves of up to three tiles (tile = wave + 8 * slot).
+// Only waves 0..7 stage query chunks and form dQ.
+template <int TPW>
+constexpr int kv_waves() { return TPW == 1 ? 16 : 8; }
 constexpr int KV_QC = 32;  // query rows per chunk
 
 __device__ __forceinline__ int row_off(int row, int chunk) {  // [32][64]
@@ -367,8 +370,10 @@ __device__ __forceinline__ int ds_off(int key, int row) {  // [KMAX][32]
 // Keys past the end need no mask: they only feed their own (discarded) dK, dV
 // columns and, with FQ, dQ through K rows that are zero in LDS.
 template <int OP, int TPW, bool FQ>
-__global__ __attribute__((amdgpu_flat_work_group_size(KV_W * 64, KV_W * 64), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kv_waves<TPW>() * 64, kv_waves<TPW>() * 64),
+                          amdgpu_waves_per_eu(kv_waves<TPW>() / 4, kv_waves<TPW>() / 4)))
 void attn_bwd_dkv_kernel(BwdParams p) {
+  constexpr int KV_W = kv_waves<TPW>();
   __shared__ __attribute__((aligned(16))) KvSmem<FQ> sm;
   KvBuf* sbuf = sm.sbuf;
 
@@ -434,12 +439,14 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   // issued by fetch(); the LSE transform waits for stage() so that no wave
   // stalls on a global load a chunk early.
   const bool carries_q = tid < 256;
+  const bool stager = tid < 512;
   const int srow = (tid & 255) >> 3, sch = tid & 7;
   bf16x8 pre = zero8(), pre_o = zero8();
   float pre_s = 0.f;
   bool pre_valid = false;
   int64_t pre_lo = 0;
   auto fetch = [&](int c) {
+    if (KV_W > 8 && !stager) return;
     // padding rows read a real (clamped) row; their LSE of +inf zeroes P
     const int r = c * KV_QC + srow;
     pre_valid = r < p.rows;
@@ -460,6 +467,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   // goes to the workspace for the dq kernel (which runs after this one), where
   // workgroups whose chunk ranges overlap write the same bits
   auto stage = [&](KvBuf& b) {
+    if (KV_W > 8 && !stager) return;
     st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
     if (carries_q) {
       if (sch == 0) b.lse[srow] = pre_valid ? pre_s * kLog2e : INFINITY;
@@ -540,6 +548,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   }
   auto dq_phase = [&](int cq) {
     if constexpr (FQ) {
+      if (KV_W > 8 && wave >= 8) return;
       const int r0q = cq * KV_QC;
       const int qlo = r0q / G, qhi = (min(r0q + KV_QC, p.rows) - 1) / G;
       int klo, khi;
@@ -798,39 +807,37 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.rows_per_split = per * DQ_QC;
   p.splits = (p.rows + p.rows_per_split - 1) / p.rows_per_split;
   const long g1 = problems * p.splits;
-  // dkv kernel: one workgroup per problem and block of at most 320 keys (the
-  // 24 tile slots of its 8 waves), blocks of equal size in whole tiles
+  // dkv kernel: one workgroup per problem and block of at most 320 keys,
+  // blocks of equal size in whole tiles
   p.kvb = (p.L + KMAX - 1) / KMAX;
   p.kbl = (((p.L + p.kvb - 1) / p.kvb) + 15) & ~15;
   const long g2 = problems * p.kvb;
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 
-  // blocks of up to 256 keys need only two tile slots per wave (fewer
-  // registers); up to 320 take three
-  const bool tpw2 = p.kbl <= KV_W * 2 * 16;
-  // one key block per problem: the dkv kernel forms dQ as well (from each
-  // chunk's dS, which it holds in LDS), and the dq kernel is not launched
+  // time attention, blocks of up to 256 keys: 16 waves of one tile; otherwise
+  // 8 waves of up to three (space attention's agent-mask state does not fit
+  // the one-tile waves' 128 registers).  One key block per problem: the dkv
+  // kernel forms dQ as well (from each chunk's dS, which it holds in LDS), and
+  // the dq kernel is not launched.
+  const bool one = d.op == OP_TIME && p.kbl <= 16 * 16;
   const bool fq = p.kvb == 1;
-  const dim3 g2d((unsigned)g2), b2d(KV_W * 64);
+  const dim3 g2d((unsigned)g2);
+  const dim3 b1(kv_waves<1>() * 64), b3(kv_waves<3>() * 64);
   if (d.op == OP_SPACE) {
-    if (fq && tpw2)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2, true>), g2d, b2d, 0, stream, p);
-    else if (fq)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, true>), g2d, b2d, 0, stream, p);
-    else if (tpw2)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2, false>), g2d, b2d, 0, stream, p);
+    if (fq)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, true>), g2d, b3, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, false>), g2d, b2d, 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, false>), g2d, b3, 0, stream, p);
     if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   } else {
-    if (fq && tpw2)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 2, true>), g2d, b2d, 0, stream, p);
+    if (fq && one)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true>), g2d, b1, 0, stream, p);
     else if (fq)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), g2d, b2d, 0, stream, p);
-    else if (tpw2)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 2, false>), g2d, b2d, 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), g2d, b3, 0, stream, p);
+    else if (one)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, false>), g2d, b1, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, false>), g2d, b2d, 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, false>), g2d, b3, 0, stream, p);
     if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   }
   return hipGetLastError();
