@@ -297,9 +297,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
 
 // ------------------------------------------------------------ dkv kernel
 
-// Key blocks of up to 256 keys: 16 waves of one 16-key tile each (four waves
-// per SIMD); up to 320: 8 waves of up to three tiles (tile = wave + 8 * slot).
-// Only waves 0..7 stage query chunks and form dQ.
+// Tile slots per wave TPW: one (16 waves, four per SIMD), two or three (8
+// waves; tile = wave + waves * slot).  Only waves 0..7 stage query chunks and
+// form dQ.
 template <int TPW>
 constexpr int kv_waves() { return TPW == 1 ? 16 : 8; }
 constexpr int KV_QC = 32;  // query rows per chunk
@@ -814,30 +814,35 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   const long g2 = problems * p.kvb;
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 
-  // time attention, blocks of up to 256 keys: 16 waves of one tile; otherwise
-  // 8 waves of up to three (space attention's agent-mask state does not fit
-  // the one-tile waves' 128 registers).  One key block per problem: the dkv
-  // kernel forms dQ as well (from each chunk's dS, which it holds in LDS), and
-  // the dq kernel is not launched.
-  const bool one = d.op == OP_TIME && p.kbl <= 16 * 16;
+  // Waves and tile slots per key block (measured): the fused time backward
+  // with blocks of up to 256 keys, 16 waves of one tile (four per SIMD; space
+  // attention's agent-mask state does not fit their 128 registers); other
+  // blocks of up to 256 keys, 8 waves of two; up to 320, 8 waves of three.
+  // One key block per problem: the dkv kernel forms dQ as well (from each
+  // chunk's dS, which it holds in LDS), and the dq kernel is not launched.
   const bool fq = p.kvb == 1;
+  const int tpw = p.kbl > 16 * 16 ? 3 : (d.op == OP_TIME && fq) ? 1 : 2;
   const dim3 g2d((unsigned)g2);
-  const dim3 b1(kv_waves<1>() * 64), b3(kv_waves<3>() * 64);
+  const dim3 bw(kv_waves<1>() * 64), b8(kv_waves<3>() * 64);
   if (d.op == OP_SPACE) {
-    if (fq)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, true>), g2d, b3, 0, stream, p);
+    if (fq && tpw == 2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2, true>), g2d, b8, 0, stream, p);
+    else if (fq)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, true>), g2d, b8, 0, stream, p);
+    else if (tpw == 2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2, false>), g2d, b8, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, false>), g2d, b3, 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, false>), g2d, b8, 0, stream, p);
     if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   } else {
-    if (fq && one)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true>), g2d, b1, 0, stream, p);
+    if (tpw == 1)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true>), g2d, bw, 0, stream, p);
     else if (fq)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), g2d, b3, 0, stream, p);
-    else if (one)
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, false>), g2d, b1, 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), g2d, b8, 0, stream, p);
+    else if (tpw == 2)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 2, false>), g2d, b8, 0, stream, p);
     else
-      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, false>), g2d, b3, 0, stream, p);
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, false>), g2d, b8, 0, stream, p);
     if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
   }
   return hipGetLastError();
