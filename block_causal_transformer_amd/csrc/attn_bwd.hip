@@ -298,8 +298,8 @@ void attn_bwd_dq_kernel(BwdParams p) {
 // ------------------------------------------------------------ dkv kernel
 
 // Tile slots per wave TPW: one (16 waves, four per SIMD), two or three (8
-// waves; tile = wave + waves * slot).  Only waves 0..7 stage query chunks and
-// form dQ.
+// waves; tile = wave + waves * slot).  Waves 0..7 form dQ; with 16 waves,
+// waves 8..15 stage the query chunks (with 8, every wave does both).
 template <int TPW>
 constexpr int kv_waves() { return TPW == 1 ? 16 : 8; }
 constexpr int KV_QC = 32;  // query rows per chunk
@@ -434,12 +434,15 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       dVT[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // staging: threads 0..255 carry Q (and LSE), threads 256..511 dO (and Delta);
+  // staging: the first 256 staging threads carry Q (and LSE), the next 256
+  // dO (and Delta);
   // a piece is (row, 16-byte column chunk) of the chunk.  The loads are only
   // issued by fetch(); the LSE transform waits for stage() so that no wave
   // stalls on a global load a chunk early.
-  const bool carries_q = tid < 256;
-  const bool stager = tid < 512;
+  // with 16 waves the staging goes to waves 8..15, which form no dQ
+  const int stid = KV_W > 8 ? tid - 512 : tid;
+  const bool carries_q = (stid & 511) < 256;
+  const bool stager = stid >= 0;
   const int srow = (tid & 255) >> 3, sch = tid & 7;
   bf16x8 pre = zero8(), pre_o = zero8();
   float pre_s = 0.f;
