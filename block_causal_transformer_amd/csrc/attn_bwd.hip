@@ -434,12 +434,11 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       dVT[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // staging: the first 256 staging threads carry Q (and LSE), the next 256
-  // dO (and Delta);
-  // a piece is (row, 16-byte column chunk) of the chunk.  The loads are only
-  // issued by fetch(); the LSE transform waits for stage() so that no wave
-  // stalls on a global load a chunk early.
-  // with 16 waves the staging goes to waves 8..15, which form no dQ
+  // staging (by waves 8..15 with 16 waves, as they form no dQ; by all 8
+  // otherwise): the first 256 staging threads carry Q (and LSE), the next 256
+  // dO (and Delta); a piece is (row, 16-byte column chunk) of the chunk.  The
+  // loads are only issued by fetch(); the LSE transform waits for stage() so
+  // that no wave stalls on a global load a chunk early.
   const int stid = KV_W > 8 ? tid - 512 : tid;
   const bool carries_q = (stid & 511) < 256;
   const bool stager = stid >= 0;
