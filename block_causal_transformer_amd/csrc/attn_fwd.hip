@@ -35,6 +35,12 @@ namespace {
 constexpr int KMAX = 320;   // keys resident in LDS per pass
 constexpr int FW = 8;       // waves per workgroup
 constexpr int QCH = 32;     // query rows per wave and chunk
+// decode: small workgroups with a small key block, so that several
+// problems (each one computing wave) share a CU and their staging overlaps
+constexpr int DEC_FW = 4;
+constexpr int DEC_KMAX = 96;
+template <int OP> constexpr int waves_of() { return OP == OP_DECODE ? DEC_FW : FW; }
+template <int OP> constexpr int keys_of() { return OP == OP_DECODE ? DEC_KMAX : KMAX; }
 constexpr int NQT = QCH / 16;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
@@ -75,10 +81,15 @@ __device__ __forceinline__ int vt_off(int d, int pos) {  // sVT: [64][KMAX]
 // ring (rollout over a KV cache); its chunks are 16 rows (a problem has G
 // rows per new frame), and it keeps V row-major in LDS, reading the PV
 // operand with transposing reads, since its staging, not its few steps,
-// dominates.
+// dominates.  For the same reason a decode workgroup is 4 waves with a
+// 96-key block (24 KB of LDS), so five problems share a CU, and each
+// thread issues all its loads of a block before its LDS stores.
 template <int OP>
-__global__ __attribute__((amdgpu_flat_work_group_size(FW * 64, FW * 64), amdgpu_waves_per_eu(4, 4)))
+__global__ __attribute__((amdgpu_flat_work_group_size(waves_of<OP>() * 64, waves_of<OP>() * 64),
+                          amdgpu_waves_per_eu(4, 4)))
 void attn_fwd_kernel(FwdParams p) {
+  constexpr int FW = waves_of<OP>();
+  constexpr int KMAX = keys_of<OP>();
   // rows per chunk: a decode problem has only G rows per new frame
   constexpr int NQ = OP == OP_DECODE ? 1 : NQT;
   constexpr int QC = 16 * NQ;
@@ -183,19 +194,39 @@ void attn_fwd_kernel(FwdParams p) {
       if (nkb > 1 || pass == 0) {
         if (nkb > 1) __syncthreads();
         const int lp = (kn + 31) & ~31;
-        for (int idx = tid; idx < lp * 8; idx += NT) {
-          const int r = idx >> 3, c = idx & 7;
-          bf16x8 kv = zero8(), vv = zero8();
-          if (r < kn) {
-            kv = ld_global16(kbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
-            vv = ld_global16(vbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
+        if constexpr (OP == OP_DECODE) {
+          // V stays row-major (laid out as K) and is read back transposed:
+          // one 16-byte write instead of eight 2-byte ones
+          constexpr int PER = KMAX * 8 / NT;
+          static_assert(PER * NT == KMAX * 8, "a block is a whole number of rounds");
+          bf16x8 kq[PER], vq[PER];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) {
+            const int idx = tid + i * NT, r = idx >> 3, c = idx & 7;
+            kq[i] = zero8();
+            vq[i] = zero8();
+            if (r < kn) {
+              kq[i] = ld_global16(kbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
+              vq[i] = ld_global16(vbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
+            }
           }
-          st_lds16(sK + k_off(r, c), kv);
-          if constexpr (OP == OP_DECODE) {
-            // decode: V stays row-major (laid out as K) and is read back
-            // transposed; one 16-byte write instead of eight 2-byte ones
-            st_lds16(sVT + k_off(r, c), vv);
-          } else {
+#pragma unroll
+          for (int i = 0; i < PER; ++i) {
+            const int idx = tid + i * NT, r = idx >> 3, c = idx & 7;
+            if (r < lp) {
+              st_lds16(sK + k_off(r, c), kq[i]);
+              st_lds16(sVT + k_off(r, c), vq[i]);
+            }
+          }
+        } else {
+          for (int idx = tid; idx < lp * 8; idx += NT) {
+            const int r = idx >> 3, c = idx & 7;
+            bf16x8 kv = zero8(), vv = zero8();
+            if (r < kn) {
+              kv = ld_global16(kbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
+              vv = ld_global16(vbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
+            }
+            st_lds16(sK + k_off(r, c), kv);
             const int pp = vt_perm(r);
 #pragma unroll
             for (int e = 0; e < 8; ++e) sVT[vt_off(c * 8 + e, pp)] = vv[e];
@@ -378,6 +409,7 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   // covers the 256 CUs (two workgroups each) about three times over.
   const long problems = (long)p.units * p.Hkv;
   const int qch = d.op == OP_DECODE ? 16 : QCH;  // rows per chunk (as in the kernel)
+  const int FW = d.op == OP_DECODE ? DEC_FW : bca::FW;  // waves per workgroup
   const int chunks = (p.rows + qch - 1) / qch;
   int splits = (int)((3 * 512 + problems - 1) / problems);
   splits = max(1, min(splits, (chunks + FW - 1) / FW));
@@ -397,7 +429,7 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   else if (d.op == OP_TIME)
     hipLaunchKernelGGL(attn_fwd_kernel<OP_TIME>, dim3((unsigned)grid), dim3(FW * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<OP_DECODE>, dim3((unsigned)grid), dim3(FW * 64), 0, stream, p);
+    hipLaunchKernelGGL(attn_fwd_kernel<OP_DECODE>, dim3((unsigned)grid), dim3(DEC_FW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
