@@ -412,9 +412,12 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   const int FW = d.op == OP_DECODE ? DEC_FW : bca::FW;  // waves per workgroup
   const int chunks = (p.rows + qch - 1) / qch;
   int splits = (int)((3 * 512 + problems - 1) / problems);
-  splits = max(1, min(splits, (chunks + FW - 1) / FW));
+  // A grid too small to fill the chip that way (one block's space attention
+  // during a rollout) is split down to 2 chunks per workgroup: more of the
+  // chip then stages K/V and computes at once (1 chunk restages too much).
+  splits = max(1, min(splits, (chunks + 1) / 2));
   int per = (chunks + splits - 1) / splits;
-  per = ((per + FW - 1) / FW) * FW;  // whole passes of FW chunks
+  if (per >= FW) per = ((per + FW - 1) / FW) * FW;  // whole passes of FW chunks
   // Windowed time attention over many frames: fewer rows per workgroup, so
   // that the keys a workgroup sees fit one LDS block (otherwise every pass
   // restages all its blocks).
