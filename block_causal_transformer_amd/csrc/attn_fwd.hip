@@ -22,7 +22,9 @@
 // with a lazy rescale (a row's running reference max is moved only when one
 // of its new scores exceeds it by more than 2^8, which keeps exp2 arguments
 // <= 8; rows never rescale because of other rows' scores);
-// O^T += V^T P^T on MFMA with V^T from LDS.  Fully masked key steps are never
+// O^T += V^T P^T on MFMA, V kept row-major in LDS (laid out as K, one 16-byte
+// write per piece when staged) and its V^T operand formed by transposing LDS
+// reads.  Fully masked key steps are never
 // visited (causal and window ranges), and per-element masks are applied only
 // on steps that straddle a mask edge.
 #include "bca_device.h"
@@ -60,30 +62,19 @@ struct FwdParams {
   int Tk, kfirst, qoff;
 };
 
-// V^T is stored with keys permuted inside each group of 32 so that the 8 keys
-// a lane feeds to one PV MFMA are contiguous: key 32a + 16h + 4g + j sits at
-// position 32a + 8g + 4h + j.
-__device__ __forceinline__ int vt_perm(int key) {
-  return (key & ~31) | (((key >> 2) & 3) << 3) | (((key >> 4) & 1) << 2) | (key & 3);
-}
-
-__device__ __forceinline__ int k_off(int row, int chunk) {  // sK: [KMAX][64], 16B chunks xor-swizzled
+// sK, sV: [KMAX][64], 16-byte pieces xor-swizzled by row
+__device__ __forceinline__ int k_off(int row, int chunk) {
   return row * 64 + ((chunk ^ (row & 7)) << 3);
-}
-
-__device__ __forceinline__ int vt_off(int d, int pos) {  // sVT: [64][KMAX]
-  return d * KMAX + ((((pos >> 3) ^ (d & 7))) << 3) + (pos & 7);
 }
 
 // 8 waves of 32 query rows; two workgroups (80 KB of LDS each) share a CU,
 // so each SIMD interleaves four waves.  OP_DECODE runs the time op's code
 // with the query positions shifted by qoff and the key frames read from a
 // ring (rollout over a KV cache); its chunks are 16 rows (a problem has G
-// rows per new frame), and it keeps V row-major in LDS, reading the PV
-// operand with transposing reads, since its staging, not its few steps,
-// dominates.  For the same reason a decode workgroup is 4 waves with a
-// 96-key block (24 KB of LDS), so five problems share a CU, and each
-// thread issues all its loads of a block before its LDS stores.
+// rows per new frame); since its staging, not its few steps, dominates, a
+// decode workgroup is 4 waves with a 96-key block (24 KB of LDS), so five
+// problems share a CU, and each thread issues all its loads of a block
+// before its LDS stores.
 template <int OP>
 __global__ __attribute__((amdgpu_flat_work_group_size(waves_of<OP>() * 64, waves_of<OP>() * 64),
                           amdgpu_waves_per_eu(4, 4)))
@@ -94,7 +85,7 @@ void attn_fwd_kernel(FwdParams p) {
   constexpr int NQ = OP == OP_DECODE ? 1 : NQT;
   constexpr int QC = 16 * NQ;
   __shared__ __attribute__((aligned(16))) bf16 sK[KMAX * 64];
-  __shared__ __attribute__((aligned(16))) bf16 sVT[64 * KMAX];
+  __shared__ __attribute__((aligned(16))) bf16 sV[KMAX * 64];
   constexpr int NT = FW * 64;
 
   int ug, split;
@@ -195,8 +186,6 @@ void attn_fwd_kernel(FwdParams p) {
         if (nkb > 1) __syncthreads();
         const int lp = (kn + 31) & ~31;
         if constexpr (OP == OP_DECODE) {
-          // V stays row-major (laid out as K) and is read back transposed:
-          // one 16-byte write instead of eight 2-byte ones
           constexpr int PER = KMAX * 8 / NT;
           static_assert(PER * NT == KMAX * 8, "a block is a whole number of rounds");
           bf16x8 kq[PER], vq[PER];
@@ -215,7 +204,7 @@ void attn_fwd_kernel(FwdParams p) {
             const int idx = tid + i * NT, r = idx >> 3, c = idx & 7;
             if (r < lp) {
               st_lds16(sK + k_off(r, c), kq[i]);
-              st_lds16(sVT + k_off(r, c), vq[i]);
+              st_lds16(sV + k_off(r, c), vq[i]);
             }
           }
         } else {
@@ -227,9 +216,7 @@ void attn_fwd_kernel(FwdParams p) {
               vv = ld_global16(vbase + (int64_t)kframe(key0 + r) * gk.pos_stride + c * 8);
             }
             st_lds16(sK + k_off(r, c), kv);
-            const int pp = vt_perm(r);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sVT[vt_off(c * 8 + e, pp)] = vv[e];
+            st_lds16(sV + k_off(r, c), vv);
           }
         }
         __syncthreads();
@@ -334,16 +321,11 @@ void attn_fwd_kernel(FwdParams p) {
         // O^T += V^T P^T
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          bf16x8 vt;
-          if constexpr (OP == OP_DECODE) {
-            // lane (li, lg) receives head dim dt*16 + li of keys 4 lg .. +3 and
-            // 16 + 4 lg .. +3 of the step, the keys its P^T operand holds
-            const int kr = st * 32 + 4 * lg + (li >> 2), dcol = dt * 16 + 4 * (li & 3);
-            vt = join8(ld_lds_tr4(sVT + k_off(kr, dcol >> 3) + (dcol & 7)),
-                       ld_lds_tr4(sVT + k_off(kr + 16, dcol >> 3) + (dcol & 7)));
-          } else {
-            vt = ld_lds16(sVT + vt_off(dt * 16 + li, st * 32 + lg * 8));
-          }
+          // lane (li, lg) receives head dim dt*16 + li of keys 4 lg .. +3 and
+          // 16 + 4 lg .. +3 of the step, the keys its P^T operand holds
+          const int kr = st * 32 + 4 * lg + (li >> 2), dcol = dt * 16 + 4 * (li & 3);
+          const bf16x8 vt = join8(ld_lds_tr4(sV + k_off(kr, dcol >> 3) + (dcol & 7)),
+                                  ld_lds_tr4(sV + k_off(kr + 16, dcol >> 3) + (dcol & 7)));
 #pragma unroll
           for (int qt = 0; qt < NQ; ++qt) acc[qt][dt] = mfma16(vt, pb[qt], acc[qt][dt]);
         }
