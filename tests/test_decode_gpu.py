@@ -4,7 +4,9 @@ state (wrapped ring) and at its first frames, several new frames at once, a
 cache larger than the window, an unbounded window longer than one LDS key
 block, 40 query heads per KV head (several row chunks per new frame),
 head_dim 32 and fp32 (the generic kernel), and decode of frame t
-against row t of the full-sequence time attention kernel."""
+against row t of the full-sequence time attention kernel; also the space
+attention of the rollout's new block, whose tiny grid the forward launcher
+splits differently from every training shape."""
 import types
 
 import numpy as np
@@ -113,3 +115,18 @@ def test_decode_graph_replays_match_eager():
         assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), "replay %d o" % r
         assert torch.equal(lse.view(torch.int32), l_ref.view(torch.int32)), "replay %d lse" % r
         ops.attn_decode_fwd(q, kc, vc, w.q_frame0, window=w.window)  # eager work between
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_rollout_space_block_matches_oracle(B):
+    """The rollout step's other half: space attention (agent isolation) over
+    the new 290-token block of each environment, forward only.  With so few
+    problems the forward launcher splits each one into 2-chunk workgroups
+    (46 per problem, the last chunk 20 rows), a grid no training shape uses."""
+    _needs_gpu()
+    w = C.get("3").with_(B=B, T=1, seed=6200 + B)
+    x = gen.make_inputs(w, with_dout=False)
+    print("rollout space block", w, flush=True)
+    got = U.run_hip(w, x, bwd=False)
+    want = U.run_oracle(w, x, bwd=False)
+    print(U.assert_close(w, got, want, "rollout space block B=%d" % B))
