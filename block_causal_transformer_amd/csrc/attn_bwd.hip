@@ -68,6 +68,7 @@ struct BwdParams {
   float scale, scale_log2, inv_g;
   int splits, rows_per_split;  // dq kernel
   int kvb, kbl;                // dkv kernel: key blocks per problem, keys per block
+  int poison;                  // debug: NaN-fill LDS before staging
 };
 
 // ------------------------------------------------------------- dq kernel
@@ -99,6 +100,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(DQ_W * 64, DQ_W * 64), amd
 void attn_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   constexpr int NT = DQ_W * 64;
+  if (p.poison) {
+    poison_lds(&sm, sizeof(sm), threadIdx.x, NT);
+    __syncthreads();
+  }
 
   int ug, split;
   xcd_remap(blockIdx.x, p.units * p.Hkv, p.splits, ug, split);
@@ -376,6 +381,10 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   constexpr int KV_W = kv_waves<TPW>();
   __shared__ __attribute__((aligned(16))) KvSmem<FQ> sm;
   KvBuf* sbuf = sm.sbuf;
+  if (p.poison) {
+    poison_lds(&sm, sizeof(sm), threadIdx.x, KV_W * 64);
+    __syncthreads();
+  }
 
   // workgroup = (problem, block of kbl keys); one block for L <= 320
   int ug, kb;
@@ -791,6 +800,7 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.scale = d.scale;
   p.scale_log2 = d.scale * kLog2e;
   p.inv_g = 1.0f / (float)p.G;
+  p.poison = d.poison;
   if (p.G > 256 || (long)p.rows >= (1L << 21)) return hipErrorInvalidValue;
   const long problems = (long)p.units * p.Hkv;
 

@@ -60,6 +60,7 @@ struct FwdParams {
   // frame kfirst + x at frame (kfirst + x) % Tk; kernel query position y sits
   // at key position y + qoff
   int Tk, kfirst, qoff;
+  int poison;  // debug: NaN-fill LDS before staging
 };
 
 // sK, sV: [KMAX][64], 16-byte pieces xor-swizzled by row
@@ -87,6 +88,11 @@ void attn_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) bf16 sK[KMAX * 64];
   __shared__ __attribute__((aligned(16))) bf16 sV[KMAX * 64];
   constexpr int NT = FW * 64;
+  if (p.poison) {
+    poison_lds(sK, sizeof(sK), threadIdx.x, NT);
+    poison_lds(sV, sizeof(sV), threadIdx.x, NT);
+    __syncthreads();
+  }
 
   int ug, split;
   if constexpr (OP == OP_TIME) {
@@ -386,6 +392,7 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.agent_count = d.agent_count;
   p.scale_log2 = d.scale * kLog2e;
   p.inv_g = 1.0f / (float)p.G;
+  p.poison = d.poison;
   if (p.G > 256 || (long)p.rows >= (1L << 21)) return hipErrorInvalidValue;
   // Split each problem's rows over several workgroups so that the grid
   // covers the 256 CUs (two workgroups each) about three times over.

@@ -53,6 +53,7 @@ struct ShortParams {
   int T, N, Hq, Hkv, G, L, R, problems;
   int window, agent_begin, agent_count;
   float scale;
+  int poison;  // debug: NaN-fill LDS before staging
 };
 
 // Sum over the PARTS lanes of a row (adjacent lanes).
@@ -120,6 +121,11 @@ __global__ __launch_bounds__(SWAVES * 64) void short_fwd_kernel(ShortParams p) {
   constexpr int PARTS = 64 / RP, DP = SD / PARTS;
   __shared__ __attribute__((aligned(16))) bf16 sK[SWAVES][LP * SD];
   __shared__ __attribute__((aligned(16))) bf16 sV[SWAVES][LP * SD];
+  if (p.poison) {
+    poison_lds(sK, sizeof(sK), threadIdx.x, SWAVES * 64);
+    poison_lds(sV, sizeof(sV), threadIdx.x, SWAVES * 64);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int prob = blockIdx.x * SWAVES + wave;
@@ -184,6 +190,16 @@ __global__ __launch_bounds__(bwd_waves(RP, LP) * 64) void short_bwd_kernel(Short
   __shared__ __attribute__((aligned(16))) bf16 sO[SWAVES][RP * SD];  // dO rows
   __shared__ float sP[SWAVES][LP * RP];                                // [key][row]
   __shared__ float sS[SWAVES][LP * RP];                                // dS, [key][row]
+  if (p.poison) {
+    constexpr int NT = SWAVES * 64;
+    poison_lds(sK, sizeof(sK), threadIdx.x, NT);
+    poison_lds(sV, sizeof(sV), threadIdx.x, NT);
+    poison_lds(sQ, sizeof(sQ), threadIdx.x, NT);
+    poison_lds(sO, sizeof(sO), threadIdx.x, NT);
+    poison_lds(sP, sizeof(sP), threadIdx.x, NT);
+    poison_lds(sS, sizeof(sS), threadIdx.x, NT);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int prob = blockIdx.x * SWAVES + wave;
@@ -309,6 +325,7 @@ ShortParams make_short(const AttnDims& d) {
   p.agent_begin = d.agent_begin;
   p.agent_count = d.agent_count;
   p.scale = d.scale;
+  p.poison = d.poison;
   return p;
 }
 

@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -59,6 +60,15 @@ int validate(int op, const bca_shape* s, const bca_mask* m, bca::AttnDims* d) {
   } else {
     if (m->causal != 1) return fail(BCA_ERR_UNSUPPORTED, "time attention must be causal (causal=%d)", m->causal);
   }
+  // the kernels fold the G query heads of a KV head into rows
+  // position * G + head of one problem
+  const int G = s->Hq / s->Hkv;
+  if (G > bca::kMaxGroup)
+    return fail(BCA_ERR_UNSUPPORTED, "%d query heads per KV head (at most %d)", G, bca::kMaxGroup);
+  const long L = op == BCA_OP_SPACE ? s->N : s->T;
+  if (L * G >= bca::kMaxFoldedRows)
+    return fail(BCA_ERR_UNSUPPORTED, "%ld positions x %d heads per KV head is %ld rows per problem "
+                "(fewer than %ld supported)", L, G, L * G, bca::kMaxFoldedRows);
   d->op = op;
   d->B = s->B;
   d->T = s->T;
@@ -83,11 +93,34 @@ int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
 }
 
 size_t workspace_bytes(const bca::AttnDims& d) {
+  if (!bca::bwd_needs_workspace(d)) return 0;
   if (bca::bwd_uses_mfma(d)) return bca::bwd_bf16_workspace_bytes(d);
   return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
 }
 
-int hip_status(hipError_t e, const char* what) {
+// Debug switches, read from the environment at every call:
+//  BCA_SYNC=1               synchronize the stream after every launch and
+//                           report a kernel fault as BCA_ERR_HIP from the call
+//  BCA_DEBUG_LDS_POISON=1   fill the attention kernels' LDS with NaN bit
+//                           patterns before staging (a read of LDS that no
+//                           thread wrote then shows up in the results)
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+bool sync_after_launch() { return env_flag("BCA_SYNC"); }
+int lds_poison() { return env_flag("BCA_DEBUG_LDS_POISON") ? 1 : 0; }
+
+// Clears an error an earlier, unrelated HIP call may have left in this
+// thread's error state, so that the check after the launch reports only the
+// launch's own.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
+int hip_status(hipError_t e, const char* what, void* stream) {
+  if (e == hipSuccess && sync_after_launch()) {
+    e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BCA_ERR_HIP, "%s (BCA_SYNC): %s", what, hipGetErrorString(e));
+  }
   if (e == hipSuccess) return BCA_OK;
   return fail(BCA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -102,10 +135,12 @@ int do_fwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
   st = check_ptrs(names, ptrs, 5);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  d.poison = lds_poison();
+  clear_stale_hip_error();
   hipError_t e = bca::uses_short(d)      ? bca::launch_attn_fwd_short(d, q, k, v, o, lse, s)
                   : bca::fwd_uses_mfma(d) ? bca::launch_attn_fwd_bf16(d, q, k, v, o, lse, s)
                                           : bca::launch_attn_fwd_generic(d, q, k, v, o, lse, s);
-  st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_fwd launch" : "time_attn_fwd launch");
+  st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_fwd launch" : "time_attn_fwd launch", stream);
   if (st == BCA_OK) g_last_error.clear();
   return st;
 }
@@ -129,6 +164,8 @@ int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
       return fail(BCA_ERR_INVALID_ARG, "workspace is NULL or not 16-byte aligned");
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  d.poison = lds_poison();
+  clear_stale_hip_error();
   // the short kernels form Delta per row themselves and leave the workspace alone
   hipError_t e = bca::uses_short(d)
                      ? bca::launch_attn_bwd_short(d, q, k, v, o, lse, dout, dq, dk, dv, s)
@@ -136,7 +173,7 @@ int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
                      ? bca::launch_attn_bwd_bf16(d, q, k, v, o, lse, dout, dq, dk, dv, workspace, s)
                      : bca::launch_attn_bwd_generic(d, q, k, v, o, lse, dout, dq, dk, dv,
                                                     static_cast<float*>(workspace), s);
-  st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_bwd launch" : "time_attn_bwd launch");
+  st = hip_status(e, op == BCA_OP_SPACE ? "space_attn_bwd launch" : "time_attn_bwd launch", stream);
   if (st == BCA_OK) g_last_error.clear();
   return st;
 }
@@ -166,10 +203,15 @@ int do_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, c
     return fail(BCA_ERR_INVALID_ARG,
                 "a cache of %d frames cannot hold the %d frames [%d, %d] the queries read",
                 cache_frames, last - first + 1, first, last);
+  if ((long)(last - first + 1) * (d.Hq / d.Hkv) >= bca::kMaxFoldedRows)
+    return fail(BCA_ERR_UNSUPPORTED, "the %d frames read x %d heads per KV head exceed the "
+                "kernels' %ld rows per problem", last - first + 1, d.Hq / d.Hkv, bca::kMaxFoldedRows);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  d.poison = lds_poison();
+  clear_stale_hip_error();
   hipError_t e = bca::fwd_uses_mfma(d) ? bca::launch_attn_fwd_bf16(d, q, kc, vc, o, lse, s)
                                        : bca::launch_attn_fwd_generic(d, q, kc, vc, o, lse, s);
-  st = hip_status(e, "time_attn_decode_fwd launch");
+  st = hip_status(e, "time_attn_decode_fwd launch", stream);
   if (st == BCA_OK) g_last_error.clear();
   return st;
 }
@@ -181,9 +223,12 @@ int validate_proj(const bca_proj_shape* s, bca::ProjDims* d) {
                 (long long)s->M, s->d_model, s->Hq, s->Hkv, s->D);
   if (s->d_model % 8 != 0 || s->D % 8 != 0)
     return fail(BCA_ERR_UNSUPPORTED, "d_model (%d) and D (%d) must be multiples of 8", s->d_model, s->D);
-  if ((double)s->M * (s->d_model > (s->Hq + 2 * s->Hkv) * s->D ? s->d_model : (s->Hq + 2 * s->Hkv) * s->D) > 4.0e15 ||
-      (s->M + 127) / 128 * (((int64_t)(s->Hq + 2 * s->Hkv) * s->D + 127) / 128) > 0x7fffffff ||
-      (int64_t)(s->Hq + 2 * s->Hkv) * s->D > (1 << 30))
+  // sizes in double first: (Hq + 2 Hkv) * D overflows 64-bit integers for
+  // the largest int32 fields
+  const double nout = ((double)s->Hq + 2.0 * s->Hkv) * s->D;
+  const double widest = nout > s->d_model ? nout : s->d_model;
+  if (nout > (double)(1 << 30) || (double)s->M * widest > 4.0e15 ||
+      ((double)s->M / 128.0 + 1.0) * (nout / 128.0 + 1.0) > 2147483647.0)
     return fail(BCA_ERR_INVALID_ARG, "projection too large");
   d->M = s->M;
   d->d_model = s->d_model;
@@ -223,9 +268,10 @@ int rmsnorm_qkv_fwd(const bca_proj_shape* shape, const void* x, const float* gai
   if (workspace_bytes < need)
     return fail(BCA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu required",
                 workspace_bytes, need);
+  clear_stale_hip_error();
   hipError_t e = bca::launch_rmsnorm_qkv(d, x, gain, eps, w_qkv, q, k, v, rstd, workspace,
                                          static_cast<hipStream_t>(stream));
-  st = hip_status(e, "rmsnorm_qkv_fwd launch");
+  st = hip_status(e, "rmsnorm_qkv_fwd launch", stream);
   if (st == BCA_OK) g_last_error.clear();
   return st;
 }
@@ -241,8 +287,9 @@ int out_proj_fwd(const bca_proj_shape* shape, const void* o, const void* w_o, co
   if (st) return st;
   if (residual && !aligned16(residual))
     return fail(BCA_ERR_INVALID_ARG, "pointer 'residual' is not 16-byte aligned");
+  clear_stale_hip_error();
   hipError_t e = bca::launch_out_proj(d, o, w_o, residual, y, static_cast<hipStream_t>(stream));
-  st = hip_status(e, "out_proj_fwd launch");
+  st = hip_status(e, "out_proj_fwd launch", stream);
   if (st == BCA_OK) g_last_error.clear();
   return st;
 }

@@ -103,6 +103,15 @@ __device__ __forceinline__ bf16x4 ld_lds_tr4(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// Debug aid: fill `bytes` (a multiple of 16) of LDS at `p` with all-ones
+// words, a NaN in both bf16 and fp32, from the `nthreads` threads of the
+// workgroup.  The caller places a barrier between this and the first staging.
+__device__ __forceinline__ void poison_lds(void* p, int bytes, int tid, int nthreads) {
+  const u32x4 nan4 = {0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+  u32x4* w = reinterpret_cast<u32x4*>(p);
+  for (int i = tid; i < bytes / 16; i += nthreads) w[i] = nan4;
+}
+
 __device__ __forceinline__ bf16x8 join8(const bf16x4& a, const bf16x4& b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }

@@ -18,6 +18,9 @@ struct AttnDims {
   // hold kv_frames frames per slot, absolute frame f at position f % kv_frames
   int kv_frames = 0;
   int q_frame0 = 0;
+  // debug: fill the kernels' LDS with NaN bit patterns before staging, so
+  // that a read of LDS no thread wrote shows up in the results
+  int poison = 0;
 };
 
 // AttnDims::op of the decode call (the kernels' OP_DECODE).
@@ -25,7 +28,9 @@ constexpr int OP_DECODE_ID = 2;
 
 // Key frames a decode call reads: [first, last] in absolute frame indices.
 inline void decode_key_range(const AttnDims& d, int& first, int& last) {
-  last = d.q_frame0 + d.T - 1;
+  // (T - 1) first: q_frame0 + T - 1 <= INT32_MAX is validated, q_frame0 + T
+  // need not fit
+  last = d.q_frame0 + (d.T - 1);
   first = (d.window > 0 && d.q_frame0 - d.window + 1 > 0) ? d.q_frame0 - d.window + 1 : 0;
 }
 
@@ -101,5 +106,23 @@ inline bool uses_short(const AttnDims& d) {
 inline bool bwd_uses_mfma(const AttnDims& d) { return d.dtype == 0 && d.D == 64; }
 
 inline bool fwd_uses_mfma(const AttnDims& d) { return d.dtype == 0 && d.D == 64; }
+
+// Positions a problem attends over: tokens (space) or frames (time).
+inline int attended_length(const AttnDims& d) { return d.op == 0 ? d.N : d.T; }
+
+// Limits of the MFMA kernels: folded rows r = position * G + head are
+// turned back into (position, head) in fp32, exact for G <= 256 and fewer
+// than 2^21 rows per problem.
+constexpr int kMaxGroup = 256;
+constexpr long kMaxFoldedRows = 1L << 21;
+
+// True when the backward needs the Delta workspace: the MFMA path whose
+// problems span more than one key block (dQ then comes from a second
+// kernel that reads Delta), and the generic VALU path.
+inline bool bwd_needs_workspace(const AttnDims& d) {
+  if (uses_short(d)) return false;
+  if (bwd_uses_mfma(d)) return attended_length(d) > kBwdKeyBlock;
+  return true;
+}
 
 }  // namespace bca

@@ -1,13 +1,17 @@
 """Check gfx950 device assembly for MFMA results read too early.
 
 hipcc leaves a number of wait states between an MFMA and the first non-MFMA
-instruction that reads its destination registers (gfx950 does not interlock
-that dependency).  On straight-line code it always leaves at least
-``MIN_STATES``; across a conditional branch that skips a block it has been
-seen to leave only one, so the consumer read the accumulator's old value and
-the kernel returned wrong, run-to-run different results.  This module walks
-every control-flow path after each MFMA (fall-through and branch targets)
-and reports any read of its destination that comes sooner.
+instruction that reads or overwrites its destination registers (gfx950 does
+not interlock those dependencies).  On straight-line code it always leaves
+at least the count in ``WAIT_STATES`` for that MFMA opcode (8 after a
+16x16x32 product, 12 after a 32x32x16 one, read off hipcc's own output);
+across a conditional branch that skips a block it has been seen to leave
+only one, so the consumer read the accumulator's old value and the kernel
+returned wrong, run-to-run different results.  This module walks every
+control-flow path after each MFMA (fall-through and branch targets) and
+reports any read (RAW) or non-MFMA write (WAW) of its destination that
+comes sooner.  An MFMA opcode missing from the table is reported as well,
+so that a new product shape cannot pass unchecked.
 
     python -m block_causal_transformer_amd.hazard_check FILE.s [...]
 
@@ -18,7 +22,14 @@ from __future__ import annotations
 import re
 import sys
 
-MIN_STATES = 8
+# Wait states hipcc leaves between each MFMA and a VALU access of its result.
+WAIT_STATES = {
+    "v_mfma_f32_16x16x32_bf16": 8,
+    "v_mfma_f32_16x16x32_f16": 8,
+    "v_mfma_f32_32x32x16_bf16": 12,
+    "v_mfma_f32_32x32x16_f16": 12,
+}
+MIN_STATES = 8  # the smallest entry (kept for callers that pass a fixed count)
 
 _STORES = ("ds_write", "global_store", "buffer_store", "scratch_store", "flat_store")
 
@@ -66,18 +77,24 @@ def _kernels(text: str):
     return out
 
 
-def check_function(lines, min_states: int = MIN_STATES):
-    """List of (mfma text, consumer text, wait states) violations."""
+def check_function(lines, min_states=None):
+    """List of (mfma text, consumer text, wait states) violations.  The
+    required count is the opcode's entry in WAIT_STATES, or ``min_states``
+    when given; an unknown MFMA opcode is itself a violation (wait states -1)."""
     ins, labels = _parse(lines)
     bad = []
     for i, (op, args, text) in enumerate(ins):
         if not op.startswith("v_mfma") or not args:
             continue
+        need = min_states if min_states is not None else WAIT_STATES.get(op.split("_e64")[0])
+        if need is None:
+            bad.append((text, "unknown MFMA opcode %s" % op, -1))
+            continue
         dst = _regs(args[0])
         stack, seen = [(i + 1, 0)], set()
         while stack:
             j, st = stack.pop()
-            if st >= min_states or j >= len(ins) or (j, st) in seen:
+            if st >= need or j >= len(ins) or (j, st) in seen:
                 continue
             seen.add((j, st))
             op2, a2, text2 = ins[j]
@@ -87,11 +104,14 @@ def check_function(lines, min_states: int = MIN_STATES):
                 if a2 and _regs(a2[0]) & dst:
                     continue
             else:
-                srcs = a2 if op2.startswith(_STORES) else a2[1:]
+                is_store = op2.startswith(_STORES)
+                srcs = a2 if is_store else a2[1:]
                 used = set()
                 for a in srcs:
                     used |= _regs(a)
-                if used & dst:
+                # RAW: a source reads the result; WAW: the destination
+                # (the first operand of every non-store) overwrites it
+                if used & dst or (not is_store and a2 and _regs(a2[0]) & dst):
                     bad.append((text, text2, st))
             nst = st + (int(a2[0], 0) + 1 if op2 == "s_nop" else 1)
             if op2 == "s_endpgm":
@@ -105,7 +125,7 @@ def check_function(lines, min_states: int = MIN_STATES):
     return bad
 
 
-def check_text(text: str, min_states: int = MIN_STATES):
+def check_text(text: str, min_states=None):
     """{kernel: violations} for every kernel with at least one."""
     res = {}
     for name, lines in _kernels(text):
@@ -115,7 +135,7 @@ def check_text(text: str, min_states: int = MIN_STATES):
     return res
 
 
-def check_file(path: str, min_states: int = MIN_STATES):
+def check_file(path: str, min_states=None):
     with open(path) as f:
         return check_text(f.read(), min_states)
 
@@ -127,7 +147,7 @@ def main(argv=None):
         res = check_file(path)
         for name, bad in res.items():
             status = 1
-            print("%s: %s: %d MFMA result read(s) within %d wait states" % (path, name, len(bad), MIN_STATES))
+            print("%s: %s: %d MFMA result access(es) too early (or unknown MFMA)" % (path, name, len(bad)))
             for mf, use, st in bad[:5]:
                 print("    %s  ->  %s  (after %d)" % (mf, use, st))
     return status

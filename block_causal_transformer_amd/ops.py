@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
 BCA_OK, BCA_ERR_INVALID_ARG, BCA_ERR_UNSUPPORTED, BCA_ERR_HIP = 0, 1, 2, 3
 BCA_BF16, BCA_F32 = 0, 1
 BCA_OP_SPACE, BCA_OP_TIME = 0, 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class BcaShape(ctypes.Structure):

@@ -49,12 +49,32 @@
  *                          the 32-bit grid / 64-bit offset limits;
  *     BCA_ERR_UNSUPPORTED  head_dim not 32 or 64, unknown dtype, causal or
  *                          window set on the space op, causal == 0 on the
- *                          time op;
- *     BCA_ERR_HIP          the HIP runtime reported a launch error.
+ *                          time op, more than 256 query heads per KV head
+ *                          (G = Hq / Hkv), or 2^21 or more rows per problem
+ *                          (attended length x G: N x G for space, T x G for
+ *                          time, frames read x G for decode);
+ *     BCA_ERR_HIP          the HIP runtime reported a launch error (any
+ *                          error already pending in the calling thread's HIP
+ *                          state is cleared first, so it is not reported).
  * bca_last_error() returns a human-readable detail of the calling thread's
  * last failure.  Work is asynchronous on `stream` (a hipStream_t; NULL = the
  * default stream); faults inside a kernel surface at the caller's next
  * synchronization.  No exception, abort or print crosses this interface.
+ *
+ * Non-finite inputs: inputs are expected to be finite.  A NaN or infinity in
+ * the data of one problem -- one (unit, KV head) pair: the q, o, dout, lse
+ * rows of its G query heads and the k, v rows of its KV head -- may leave
+ * that problem's outputs NaN, infinite or meaningless; the outputs of every
+ * other problem are exactly those of a run without it, and nothing faults.
+ *
+ * Debug switches (environment variables, read at every call; not for use
+ * under stream capture):
+ *     BCA_SYNC=1              every call synchronizes its stream after the
+ *                             launch and returns BCA_ERR_HIP if a kernel
+ *                             faulted;
+ *     BCA_DEBUG_LDS_POISON=1  the attention kernels fill their LDS with NaN
+ *                             bit patterns before staging, so that a read of
+ *                             LDS no thread wrote shows up in the results.
  */
 #ifndef BCA_H
 #define BCA_H
@@ -66,7 +86,7 @@
 extern "C" {
 #endif
 
-#define BCA_ABI_VERSION 3
+#define BCA_ABI_VERSION 4
 
 typedef enum {
   BCA_OK = 0,
@@ -153,11 +173,14 @@ int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const voi
                          const void* k_cache, const void* v_cache, int32_t cache_frames,
                          int32_t q_frame0, void* o, float* lse, void* stream);
 
-/* Bytes of device workspace the backward of `op` needs for `shape`: one fp32
- * Delta = rowsum(dO * O) per (query, head), i.e. B*T*N*Hq*4 bytes.  Returns 0
- * for an invalid shape.  (The backward only writes it when the attended
- * sequence, N for space and T for time, is longer than 320; callers pass it
- * regardless.) */
+/* Bytes of device workspace the backward of `op` (BCA_OP_SPACE or
+ * BCA_OP_TIME) needs for `shape`: 0 when the attended length (N for space, T
+ * for time) is at most 320 on the bf16 head_dim-64 path (every problem is one
+ * key block and one kernel forms dQ, dK and dV), else one fp32
+ * Delta = rowsum(dO * O) per (query, head), B*T*N*Hq*4 bytes, which the
+ * backward's first kernel writes and its second reads.  The op is an
+ * argument because the attended length depends on it.  Returns 0 for an
+ * invalid shape or op. */
 size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape);
 
 /* ---- projections beside attention ----

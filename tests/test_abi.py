@@ -124,9 +124,19 @@ def test_mask_descriptor_rules(lib):
 
 
 def test_workspace_query_and_check(lib):
-    # every backward path: one fp32 Delta per (query, head)
-    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=290)) == 1 * 4 * 290 * 4 * 4
-    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=256)) == 1 * 256 * 10 * 4 * 4
+    # one key block per problem (at most 320 positions): the fused MFMA
+    # backward and the short kernels need no workspace
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=290)) == 0
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=256)) == 0
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=320)) == 0
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=16, N=1432, Hq=16, Hkv=16)) == 0
+    # longer problems: one fp32 Delta per (query, head)
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=321)) == 1 * 4 * 321 * 4 * 4
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=1024)) == 1 * 1024 * 10 * 4 * 4
+    # the space op's length is N and the time op's T
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(N=1432, T=8)) == 0
+    # the generic VALU path (head_dim 32, fp32) always uses it
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(D=32)) == 1 * 4 * 10 * 4 * 4
     s = good_shape(N=1432, T=2)
     need = ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, s)
     assert need == 1 * 2 * 1432 * 4 * 4
@@ -250,3 +260,25 @@ def test_projection_rejects_bad_arguments(lib):
 def test_projection_too_large(lib):
     assert qkv_call(proj_shape(M=2 ** 40), ws_bytes=2 ** 62) == ops.BCA_ERR_INVALID_ARG
     assert "too large" in ops.bca_last_error()
+
+
+def test_size_limits_of_the_kernels_are_validated(lib):
+    """Shapes past the kernels' folded-row limits (G <= 256 query heads per KV
+    head, fewer than 2^21 rows position * G + head per problem) are refused
+    by validation with UNSUPPORTED, before any launch."""
+    for op, m in (("space", ops.BcaMask(0, 0, 0, 0, 0.0)), ("time", TIME_MASK)):
+        assert fwd_call(op, good_shape(Hq=257, Hkv=1), m) == ops.BCA_ERR_UNSUPPORTED
+        assert "per KV head" in ops.bca_last_error()
+        assert bwd_call(op, good_shape(Hq=514, Hkv=2), m) == ops.BCA_ERR_UNSUPPORTED
+    # G = 256 with 2^13 positions is exactly 2^21 rows: refused; one fewer passes validation
+    assert fwd_call("space", good_shape(N=8192, Hq=256, Hkv=1), ops.BcaMask(0, 0, 0, 0, 0.0)) \
+        == ops.BCA_ERR_UNSUPPORTED
+    assert "rows per problem" in ops.bca_last_error()
+    assert fwd_call("time", good_shape(T=69906, Hq=30, Hkv=1), TIME_MASK) == ops.BCA_ERR_UNSUPPORTED
+    assert bwd_call("time", good_shape(T=69906, Hq=30, Hkv=1), TIME_MASK) == ops.BCA_ERR_UNSUPPORTED
+    # the workspace query returns 0 for a shape the calls refuse
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(Hq=257, Hkv=1)) == 0
+    # decode: the frames read times G is the per-problem row count
+    shape = good_shape(T=1, Hq=256, Hkv=1)
+    assert decode_call(shape, ops.make_mask("time", window=0), 9000, 8191) == ops.BCA_ERR_UNSUPPORTED
+    assert "rows per problem" in ops.bca_last_error()

@@ -55,3 +55,40 @@ def test_built_kernels_pass():
         pytest.skip("no device assembly built")
     for f in files:
         assert H.check_file(f) == {}, f
+
+
+def test_32x32_product_needs_twelve_wait_states():
+    text = """k:
+\tv_mfma_f32_32x32x16_bf16 v[4:19], v[0:3], v[20:23], 0
+\ts_nop 7
+\tv_mul_f32_e32 v30, v12, v4
+\ts_endpgm
+"""
+    bad = H.check_text(text)
+    assert "k" in bad and bad["k"][0][2] == 8, bad
+    assert H.check_text(text.replace("s_nop 7", "s_nop 11")) == {}
+
+
+def test_valu_write_to_result_in_flight_is_flagged():
+    text = """k:
+\tv_mfma_f32_16x16x32_bf16 v[4:7], v[0:3], v[8:11], 0
+\ts_nop 3
+\tv_mov_b32_e32 v5, 0
+\ts_nop 7
+\tv_mul_f32_e32 v30, v12, v4
+\ts_endpgm
+"""
+    bad = H.check_text(text)
+    assert "k" in bad and "v_mov_b32" in bad["k"][0][1] and bad["k"][0][2] == 4, bad
+    assert H.check_text(text.replace("s_nop 3", "s_nop 7")) == {}
+
+
+def test_unknown_mfma_opcode_fails():
+    text = """k:
+\tv_mfma_f32_4x4x4_16b_f16 v[4:7], v[0:1], v[8:9], 0
+\ts_nop 15
+\tv_mul_f32_e32 v30, v12, v4
+\ts_endpgm
+"""
+    bad = H.check_text(text)
+    assert "k" in bad and "unknown MFMA" in bad["k"][0][1]
