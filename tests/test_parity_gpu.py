@@ -54,8 +54,6 @@ def test_parity_reduced(name):
 FULL_SAMPLES = {
     "2s": [0, 77, 511],
     "2t": [0, 300, 591],
-    "3": [0, 131, 255],
-    "4": [0, 145, 289],
     "5a": [0, 15],
     "5b": [7],
     "5c": [0, 700, 1431],
@@ -73,6 +71,28 @@ def test_parity_full_size_sampled(name):
     ws, inp_s, got_s = U.sample_units(w, got, inp, FULL_SAMPLES[name])
     want = U.run_oracle(ws, inp_s)
     print(U.assert_close(ws, got_s, want, name + " full"))
+
+
+@pytest.mark.parametrize("name", ["3", "4"])
+def test_parity_full_size_whole_tensors(name):
+    """The Minecraft space and time layers at full size, in the bench's launch
+    configuration, compared element by element on every output tensor (the
+    oracle runs OpenMP over the host's cores).  Over the 22 million dK and dV
+    elements of the time layer, an exact computation with only the method's
+    bf16 operand roundings already lands up to 0.027 (dK) and 0.023 (dV)
+    beyond the output's rounding from the fp64 result; the stored floor
+    (tests/golden/precision_floor.json) moves those two max-abs bars to the
+    floor plus 2e-3.  With BCA_PARITY_REPORT set, each tensor's figures are
+    appended to that file as JSON lines."""
+    _needs_gpu()
+    w = C.get(name)
+    print("case whole", name, flush=True)
+    inp = gen.make_inputs(w)
+    got = U.run_hip(w, inp)
+    want = U.run_oracle(w, inp)
+    floor = U.load_floor(name)
+    assert floor is not None, "no stored precision floor for " + name
+    print(U.assert_close(w, got, want, name + " whole", floor=floor))
 
 
 RAGGED = []
