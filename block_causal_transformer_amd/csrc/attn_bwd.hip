@@ -43,6 +43,8 @@
 // that the causal / window ranges make invisible are never visited.  For
 // long problems the split costs two more matmul passes (S and dP are formed
 // in both kernels) in exchange for no cross-workgroup sum of dQ.
+#include <mutex>
+
 #include "bca_device.h"
 #include "bca_kernels.h"
 
@@ -770,6 +772,38 @@ void attn_bwd_dkv_kernel(BwdParams p) {
 
 size_t bwd_bf16_workspace_bytes(const AttnDims& d) {
   return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
+}
+
+// ------------------------------------------------- static scratch (no-alloc)
+
+// Device memory of the no-allocation backward: the Delta workspace lives in
+// this file-scope array instead of a caller's buffer.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code the
+// array's name is only a stand-in; its device address on the current device
+// comes from hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k, const void* v,

@@ -178,6 +178,33 @@ int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
   return st;
 }
 
+// The backward with its workspace taken from the library's static device
+// scratch: allocates nothing (no hipMalloc, no library allocation).
+int do_bwd_noalloc(int op, const bca_shape* shape, const bca_mask* mask, const void* q,
+                   const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* stream) {
+  bca::AttnDims d;
+  int st = validate(op, shape, mask, &d);
+  if (st) return st;
+  const char* names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"};
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  st = check_ptrs(names, ptrs, 9);
+  if (st) return st;
+  const size_t need = workspace_bytes(d);
+  if (need > bca::kNoAllocScratchBytes)
+    return fail(BCA_ERR_INVALID_ARG,
+                "this shape needs %zu bytes of workspace; the static scratch holds %zu "
+                "(at most %zu query-head rows)", need, bca::kNoAllocScratchBytes,
+                bca::kNoAllocScratchBytes / sizeof(float));
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = bca::noalloc_scratch(&ws);
+    if (e != hipSuccess)
+      return fail(BCA_ERR_HIP, "static scratch lookup: %s", hipGetErrorString(e));
+  }
+  return do_bwd(op, shape, mask, q, k, v, o, lse, dout, dq, dk, dv, ws, need, stream);
+}
+
 int do_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* kc,
                   const void* vc, int32_t cache_frames, int32_t q_frame0, void* o, float* lse,
                   void* stream) {
@@ -322,6 +349,12 @@ int time_attn_bwd(const bca_shape* shape, const bca_mask* mask, const void* q, c
                   void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   return do_bwd(BCA_OP_TIME, shape, mask, q, k, v, o, lse, dout, dq, dk, dv, workspace,
                 workspace_bytes, stream);
+}
+
+int time_attn_bwd_noalloc(const bca_shape* shape, const bca_mask* mask, const void* q,
+                          const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* stream) {
+  return do_bwd_noalloc(BCA_OP_TIME, shape, mask, q, k, v, o, lse, dout, dq, dk, dv, stream);
 }
 
 size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape) {

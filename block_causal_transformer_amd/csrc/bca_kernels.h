@@ -65,6 +65,14 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
 // (query, head), written by its first kernel and read by its second.
 size_t bwd_bf16_workspace_bytes(const AttnDims& d);
 
+// Size of the static device scratch of the no-allocation backward (the
+// Delta workspace, one fp32 per (query, head)): 64 MiB, i.e. up to 2^24
+// (query, head) rows per call.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+// Device address of that scratch on the current device (looked up once per
+// device with hipGetSymbolAddress and kept); allocates nothing.
+hipError_t noalloc_scratch(void** ptr);
+
 // Generic VALU kernels: fp32 or bf16 storage, D = 32 or 64, any length.
 hipError_t launch_attn_fwd_generic(const AttnDims& d, const void* q, const void* k,
                                    const void* v, void* o, float* lse, hipStream_t stream);

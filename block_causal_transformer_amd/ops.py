@@ -7,7 +7,7 @@ library is not built, or a call fails, an exception is raised.
 
 Raw entry points carry the C names and arguments:
 ``space_attn_fwd``, ``space_attn_bwd``, ``time_attn_fwd``, ``time_attn_bwd``,
-``time_attn_decode_fwd``, ``rmsnorm_qkv_fwd``, ``out_proj_fwd``,
+``time_attn_bwd_noalloc``, ``time_attn_decode_fwd``, ``rmsnorm_qkv_fwd``, ``out_proj_fwd``,
 ``bca_bwd_workspace_bytes``, ``bca_qkv_workspace_bytes``, ``bca_status_string``,
 ``bca_last_error``, ``bca_abi_version``.  ``attn_fwd`` / ``attn_bwd`` /
 ``attn_decode_fwd`` / ``qkv_proj`` / ``out_proj`` allocate the outputs with
@@ -56,7 +56,7 @@ _lock = threading.Lock()
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTED = ["space_attn_fwd", "space_attn_bwd", "time_attn_fwd", "time_attn_bwd",
-            "time_attn_decode_fwd", "rmsnorm_qkv_fwd", "out_proj_fwd", "bca_bwd_workspace_bytes",
+            "time_attn_bwd_noalloc", "time_attn_decode_fwd", "rmsnorm_qkv_fwd", "out_proj_fwd", "bca_bwd_workspace_bytes",
             "bca_qkv_workspace_bytes", "bca_status_string", "bca_last_error", "bca_abi_version"]
 
 
@@ -81,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             f = getattr(h, name)
             f.argtypes = [SP, MP, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
             f.restype = ctypes.c_int
+        h.time_attn_bwd_noalloc.argtypes = [SP, MP, P, P, P, P, P, P, P, P, P, P]
+        h.time_attn_bwd_noalloc.restype = ctypes.c_int
         h.time_attn_decode_fwd.argtypes = [SP, MP, P, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P]
         h.time_attn_decode_fwd.restype = ctypes.c_int
         PP = ctypes.POINTER(BcaProjShape)
@@ -146,6 +148,13 @@ def time_attn_bwd(shape: BcaShape, mask: BcaMask, q, k, v, o, lse, dout, dq, dk,
     return load().time_attn_bwd(_ref(shape), _ref(mask), _ptr(q), _ptr(k),
                                 _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                 _ptr(dv), _ptr(workspace), workspace_bytes, stream)
+
+
+def time_attn_bwd_noalloc(shape: BcaShape, mask: BcaMask, q, k, v, o, lse, dout, dq, dk, dv,
+                          stream=None) -> int:
+    return load().time_attn_bwd_noalloc(_ref(shape), _ref(mask), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                        _ptr(dv), stream)
 
 
 def time_attn_decode_fwd(shape: BcaShape, mask: BcaMask, q, k_cache, v_cache, cache_frames: int,

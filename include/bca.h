@@ -173,6 +173,23 @@ int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const voi
                          const void* k_cache, const void* v_cache, int32_t cache_frames,
                          int32_t q_frame0, void* o, float* lse, void* stream);
 
+/* time_attn_bwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results as time_attn_bwd, with the workspace
+ * taken from a static device array of the library instead of an argument.
+ * It calls no hipMalloc, hipFree or allocating library routine.  The array
+ * holds 64 MiB per GPU (kept until the process ends), enough for
+ * B*T*N*Hq <= 2^24 (query, head) rows; shapes that need more workspace
+ * (bca_bwd_workspace_bytes(BCA_OP_TIME, shape) > 64 MiB) are refused with
+ * BCA_ERR_INVALID_ARG before any launch.  Every call on one GPU uses that
+ * GPU's one array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialized by the caller.  Nothing in the
+ * array needs to start at any value.  Other arguments, ownership and errors
+ * as time_attn_bwd. */
+int time_attn_bwd_noalloc(const bca_shape* shape, const bca_mask* mask, const void* q,
+                          const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* stream);
+
 /* Bytes of device workspace the backward of `op` (BCA_OP_SPACE or
  * BCA_OP_TIME) needs for `shape`: 0 when the attended length (N for space, T
  * for time) is at most 320 on the bf16 head_dim-64 path (every problem is one

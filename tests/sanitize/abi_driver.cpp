@@ -63,6 +63,12 @@ hipError_t launch_out_proj(const ProjDims&, const void*, const void*, const void
   ++g_launches;
   return hipSuccess;
 }
+static int g_lookups = 0;
+hipError_t noalloc_scratch(void** ptr) {
+  ++g_lookups;
+  *ptr = reinterpret_cast<void*>(0x20000);
+  return hipSuccess;
+}
 }  // namespace bca
 
 static int fails = 0;
@@ -182,6 +188,24 @@ int main() {
     }
     bca_proj_shape b = {1, INT_MAX - 7, INT_MAX, INT_MAX, INT_MAX - 7};
     EXPECT(out_proj_fwd(&b, P, P, nullptr, P, nullptr) != BCA_OK);
+  }
+  // the no-allocation backward: scratch only when the shape needs a workspace,
+  // refused past the static array's size
+  {
+    const bca_shape sl = {1, 1024, 290, 30, 3, 64, BCA_BF16};  // 35.6 MB of Delta
+    before = g_launches;
+    EXPECT(time_attn_bwd_noalloc(&sl, &mt, P, P, P, P, static_cast<float*>(P), P, P, P, P, nullptr) == BCA_OK);
+    EXPECT(g_launches == before + 1 && bca::g_lookups == 1);
+    EXPECT(time_attn_bwd_noalloc(&s3, &mt, P, P, P, P, static_cast<float*>(P), P, P, P, P, nullptr) == BCA_OK);
+    EXPECT(bca::g_lookups == 1);  // 256 frames: one key block, no workspace
+    const bca_shape sh = {1, 1024, 1000, 30, 3, 64, BCA_BF16};  // 123 MB of Delta
+    EXPECT(time_attn_bwd_noalloc(&sh, &mt, P, P, P, P, static_cast<float*>(P), P, P, P, P, nullptr) ==
+           BCA_ERR_INVALID_ARG);
+    EXPECT(strstr(bca_last_error(), "static scratch") != nullptr);
+    EXPECT(time_attn_bwd_noalloc(&sl, &mt, P, nullptr, P, P, static_cast<float*>(P), P, P, P, P, nullptr) ==
+           BCA_ERR_INVALID_ARG);
+    EXPECT(time_attn_bwd_noalloc(&sl, &ms, P, P, P, P, static_cast<float*>(P), P, P, P, P, nullptr) ==
+           BCA_ERR_UNSUPPORTED);
   }
   // BCA_SYNC synchronizes after a launch; status strings
   setenv("BCA_SYNC", "1", 1);
