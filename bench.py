@@ -53,11 +53,13 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 TRAFFIC_FILE_DECODE = os.path.join(ROOT, "profiles", "hbm_traffic_rollout_decode.txt")
 TRAFFIC_FILE_PROJ = os.path.join(ROOT, "profiles", "hbm_traffic_projections.txt")
+UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_utilisation.txt")
 
 
 # kernel launches of each attention call (template argument 0 = space, 1 = time)
 KERNELS = {
     "time_decode": "attn_fwd_kernel<2>",
+    "time_decode_same_ring": "attn_fwd_kernel<2>",
     "space_fwd_block": "attn_fwd_kernel<0>",
     "space_fwd": "attn_fwd_kernel<0>",
     "time_fwd": "attn_fwd_kernel<1>",
@@ -73,6 +75,35 @@ def source_digest(files=None) -> str:
     comments and layout ignored: the one the counter summaries carry."""
     from block_causal_transformer_amd.rocprof_summary import source_digest as digest
     return digest(files)
+
+
+def _read_summary(path: str):
+    """key=value pairs of a committed counter summary, or None when absent or
+    taken on kernel sources other than the current ones."""
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if "=" in line:
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    files = vals.get("source_files")
+    if vals.get("source_sha") != source_digest(files.split(",") if files else None):
+        return None
+    return vals
+
+
+def read_util(kernel_key: str, path: str = UTIL_FILE):
+    """MFMA / VALU busy figures of ``kernel_key`` from the committed rocprofv3
+    utilisation summary, or None (absent, or other kernel sources)."""
+    vals = _read_summary(path)
+    if not vals or kernel_key + ".mfma_busy_pct" not in vals:
+        return None
+    return {k: float(vals[kernel_key + "." + k]) for k in
+            ("mfma_busy_pct", "valu_busy_pct", "coexec_pct", "lds_active_pct")
+            if kernel_key + "." + k in vals}
 
 
 def read_traffic(kernel_key: str, path: str = TRAFFIC_FILE):
@@ -195,45 +226,60 @@ def main_decode(args):
     ws = C.get("3").with_(B=B, T=1)
     xd, xs = gen.make_decode_inputs(wd), gen.make_inputs(ws, with_dout=False)
     t = lambda a: torch.from_numpy(a).to(dev).to(torch.bfloat16)
-    dq, dk, dvv = t(xd["q"]), t(xd["k_cache"]), t(xd["v_cache"])
-    sq, sk, sv = t(xs["q"]), t(xs["k"]), t(xs["v"])
-    do, dl = torch.empty_like(dq), torch.empty(dq.shape[:4], dtype=torch.float32, device=dev)
-    so, sl = torch.empty_like(sq), torch.empty(sq.shape[:4], dtype=torch.float32, device=dev)
-    dshape, dmask = ops.make_shape(dq, dk), ops.make_mask("time", window=wd.window)
-    sshape, smask = ops.make_shape(sq, sk), ops.make_mask("space", **ops.workload_kwargs(ws))
+    # A rollout keeps one K/V ring per time layer (seven for the dynamics
+    # model), ~43 MB each per environment: together more than the 256 MB
+    # MALL.  The timed step therefore rotates over RINGS independent copies
+    # of the inputs (8 x 43 MB = 343 MB at one environment), so every call
+    # reads its ring from HBM as the layers of a rollout would; the same-ring
+    # figure (one ring re-read, resident in the MALL) is reported beside it.
+    RINGS = 8
+    dq = [t(xd["q"]) for _ in range(RINGS)]
+    dk = [t(xd["k_cache"]) for _ in range(RINGS)]
+    dvv = [t(xd["v_cache"]) for _ in range(RINGS)]
+    sq = [t(xs["q"]) for _ in range(RINGS)]
+    sk = [t(xs["k"]) for _ in range(RINGS)]
+    sv = [t(xs["v"]) for _ in range(RINGS)]
+    do = [torch.empty_like(dq[0]) for _ in range(RINGS)]
+    dl = [torch.empty(dq[0].shape[:4], dtype=torch.float32, device=dev) for _ in range(RINGS)]
+    so = [torch.empty_like(sq[0]) for _ in range(RINGS)]
+    sl = [torch.empty(sq[0].shape[:4], dtype=torch.float32, device=dev) for _ in range(RINGS)]
+    dshape, dmask = ops.make_shape(dq[0], dk[0]), ops.make_mask("time", window=wd.window)
+    sshape, smask = ops.make_shape(sq[0], sk[0]), ops.make_mask("space", **ops.workload_kwargs(ws))
     stream = torch.cuda.current_stream()
-    sp = stream.cuda_stream
 
-    # A generation step is two small launches, so it is captured once in a
-    # HIP graph and replayed (the ABI calls take the capturing stream).
-    def space_op():
+    # A generation step is two small launches, so it is captured in a HIP
+    # graph and replayed (the ABI calls take the capturing stream).
+    def space_op(i=0):
         cs = torch.cuda.current_stream().cuda_stream
-        if ops.space_attn_fwd(sshape, smask, sq, sk, sv, so, sl, cs):
+        if ops.space_attn_fwd(sshape, smask, sq[i], sk[i], sv[i], so[i], sl[i], cs):
             raise RuntimeError(ops.bca_last_error())
 
-    def decode_op():
+    def decode_op(i=0):
         cs = torch.cuda.current_stream().cuda_stream
-        if ops.time_attn_decode_fwd(dshape, dmask, dq, dk, dvv, wd.cache_frames, wd.q_frame0,
-                                    do, dl, cs):
+        if ops.time_attn_decode_fwd(dshape, dmask, dq[i], dk[i], dvv[i], wd.cache_frames,
+                                    wd.q_frame0, do[i], dl[i], cs):
             raise RuntimeError(ops.bca_last_error())
 
-    def step():
-        space_op()
-        decode_op()
+    def step(i=0):
+        space_op(i)
+        decode_op(i)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i % RINGS)
     torch.cuda.synchronize()
-    # per-op durations: graphs of REPS back-to-back launches of one op, so the
-    # graph launch itself is amortized (the launches rewrite the same outputs)
-    REPS = 20
+    # graphs: "steps" = RINGS consecutive steps over the rotated copies; per
+    # op, REPS back-to-back launches (rotated, and on one copy), so the graph
+    # launch itself is amortized
+    REPS = 24
     graphs = {}
-    for key, fn, reps in (("step", step, 1), ("space_fwd_block", space_op, REPS),
-                          ("time_decode", decode_op, REPS)):
+    for key, fn, reps, rot in (("steps", step, RINGS, True),
+                               ("space_fwd_block", space_op, REPS, True),
+                               ("time_decode", decode_op, REPS, True),
+                               ("time_decode_same_ring", decode_op, REPS, False)):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(reps):
-                fn()
+            for r in range(reps):
+                fn(r % RINGS if rot else 0)
         graphs[key] = g
         for _ in range(3):
             g.replay()
@@ -249,13 +295,15 @@ def main_decode(args):
         return e0.elapsed_time(e1) / n
 
     op_ms = {k: timed(graphs[k], max(1, args.steps // REPS)) / REPS
-             for k in ("space_fwd_block", "time_decode")}
+             for k in ("space_fwd_block", "time_decode", "time_decode_same_ring")}
     torch.cuda.synchronize()
+    replays = max(1, args.steps // RINGS)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graphs["step"].replay()
+    for _ in range(replays):
+        graphs["steps"].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    args.steps = replays * RINGS
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -266,16 +314,18 @@ def main_decode(args):
 
     ops_ = {}
     for key, fl, by in (("space_fwd_block", C.flops(ws, "fwd"), C.min_bytes(ws, "fwd")),
-                        ("time_decode", C.decode_flops(wd), C.decode_min_bytes(wd))):
+                        ("time_decode", C.decode_flops(wd), C.decode_min_bytes(wd)),
+                        ("time_decode_same_ring", C.decode_flops(wd), C.decode_min_bytes(wd))):
         ms = op_ms[key]
         ops_[key] = {"ms": round(ms, 5), "tflops": round(fl / ms / 1e9, 2),
                      "gbps": round(by / ms / 1e6, 1),
                      "pct_hbm_peak": round(100.0 * by / ms / 1e6 / PEAK_HBM_GBPS, 2),
                      "flop": fl, "min_bytes": by}
-    dom = max(ops_, key=lambda k: ops_[k]["ms"])
+    # the dominant op of the (rotated) step; the same-ring figure is context
+    dom = max(("space_fwd_block", "time_decode"), key=lambda k: ops_[k]["ms"])
     d = ops_[dom]
     roof = roofline_of(d["flop"], d["min_bytes"], d["ms"])
-    roof["kernel"] = dom + " (" + KERNELS[dom] + ")"
+    roof["kernel"] = dom + " (" + KERNELS[dom] + ", ring rotated over %d copies)" % RINGS
     # the committed counters were taken on the one-environment step
     roof["traffic"] = read_traffic(dom, TRAFFIC_FILE_DECODE) if B == 1 else None
     ms_step = elapsed / args.steps * 1e3
@@ -292,8 +342,11 @@ def main_decode(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "timing": "HIP graph replays: one graph per step for value; per-op figures from graphs "
-                  "of 20 back-to-back launches of the op",
+        "timing": "HIP graph replays of %d consecutive steps, each on its own copy of the inputs "
+                  "(8 rings of 43 MB per environment, more than the 256 MB MALL, as the seven "
+                  "time layers of a rollout keep); per-op figures from graphs of %d back-to-back "
+                  "launches rotated the same way; time_decode_same_ring re-reads one ring "
+                  "(MALL-resident), context only" % (RINGS, REPS),
         "config": {
             "workload": "Minecraft rollout decode step: space attention of the new 290-token "
                         "block (30 q / 3 kv heads, d 64, agent isolation) + time attention of its "
@@ -609,6 +662,10 @@ def main_step(args):
     roof = roofline_of(d["flop"], d["min_bytes"], d["ms"])
     roof["kernel"] = dom + " (" + KERNELS[d["op"]] + ")"
     roof["traffic"] = read_traffic(dom) if args.workload == "train_step" else None
+    if args.workload == "train_step":
+        # rocprofv3 counters of the same kernels (MFMA busy share of the
+        # SIMDs' cycles), from the committed summary when it matches the sources
+        roof["counters"] = read_util(dom)
 
     cfg = {"workload": desc}
     for w in wls:

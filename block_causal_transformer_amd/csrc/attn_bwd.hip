@@ -28,9 +28,13 @@
 //             Staging a chunk also forms its rows' Delta from dO and O.
 //             When the problem's keys fit one block (at most 320: every
 //             dynamics shape), the kernel also forms dQ: each chunk's dS
-//             goes to LDS, and during the next chunk every wave forms one
-//             16 x 16 block of that chunk's dQ^T = K^T dS^T from it and an LDS
-//             copy of K.  The dq kernel is then not launched.
+//             goes to LDS, and during the next chunk that chunk's
+//             dQ^T = K^T dS^T is formed from it and an LDS copy of K: by
+//             every wave as one 16 x 16 block, or, for blocks of more than
+//             256 keys (three tile slots), by two dedicated waves as two
+//             32 x 32 blocks on v_mfma_f32_32x32x16_bf16 (half the operand
+//             reads per product), those two waves keeping one key tile each.
+//             The dq kernel is then not launched.
 //  dq kernel  (query-parallel, laid out like the forward; longer problems
 //             only): a workgroup holds K, V and K^T of one (unit, KV head)
 //             problem's key block in LDS; each wave owns 32 query rows
@@ -311,6 +315,21 @@ template <int TPW>
 constexpr int kv_waves() { return TPW == 1 ? 16 : 8; }
 constexpr int KV_QC = 32;  // query rows per chunk
 
+// With the query gradient formed by waves 6 and 7 on 32x32 products (DQ32:
+// one key block per problem, three tile slots), those two waves keep one key
+// tile each and waves 0..5 up to three: slot 0 holds tiles 0..7 (wave w has
+// tile w), slot 1 tiles 8..13 and slot 2 tiles 14..19 (waves 0..5), so a
+// block of up to 320 keys is covered.  Otherwise tile = wave + waves * slot.
+template <int KV_W, bool DQ32>
+__device__ __forceinline__ int tile_of(int wave, int m) {
+  if constexpr (DQ32) {
+    if (m == 0) return wave;
+    return wave < 6 ? 8 + 6 * (m - 1) + wave : 1 << 20;
+  } else {
+    return wave + KV_W * m;
+  }
+}
+
 __device__ __forceinline__ int row_off(int row, int chunk) {  // [32][64]
   return row * 64 + ((chunk ^ (row & 7)) << 3);
 }
@@ -410,13 +429,15 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   // (keys past the end read as zero); with FQ and three tiles the K operands
   // are read from the LDS copy of K at each use instead (register pressure)
   constexpr bool KB_LDS = FQ && TPW >= 3;
+  constexpr bool DQ32 = FQ && TPW == 3;
+  auto tile = [&](int m) { return tile_of<KV_W, DQ32>(wave, m); };
   bf16x8 KB[KB_LDS ? 1 : TPW][2], VB[TPW][2];
   int keyG[TPW];    // time: key * G
   bool kagent[TPW];  // space: the lane's key is an agent key
   bool keyok[TPW];
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
-    const int key = kb0 + (wave + KV_W * m) * 16 + li;
+    const int key = kb0 + tile(m) * 16 + li;
     const bool ok = key < kend;
     const int64_t off = gk.base + (int64_t)min(key, p.L - 1) * gk.pos_stride + g * 64;
 #pragma unroll
@@ -588,6 +609,70 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       }
     }
   };
+  // DQ32: wave 6 + a forms the 32 x 32 block of the chunk's dQ^T for head
+  // dims 32a .. 32a + 31 (all 32 rows) on v_mfma_f32_32x32x16_bf16, over
+  // 16-key steps.  Operand layout: lane l holds row l % 32 of A (head dim)
+  // and column l % 32 of B (query row) for contraction indices (keys)
+  // 8 (l / 32) .. +7, each as two transposing reads of 4 keys; the output
+  // lane l holds query row l % 32, head dims 8 q + 4 (l / 32) + j (q, j <
+  // 4) of the block.
+  int oK32[2] = {0, 0}, oD32[2] = {0, 0};
+  if constexpr (DQ32) {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int kq = 8 * (g16 >> 1) + (i16 >> 2);  // key of this lane's piece (+4 for the second)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      oK32[e] = kq_off(kq + 4 * e, 32 * (wave & 1) + 16 * (g16 & 1) + 4 * (i16 & 3));
+      oD32[e] = ds_off(kq + 4 * e, 16 * (g16 & 1) + 4 * (i16 & 3));
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) asm volatile("" : "+v"(oK32[e]), "+v"(oD32[e]));
+  }
+  auto dq_phase32 = [&](int cq) {
+    if constexpr (DQ32) {
+      if (wave < 6) return;
+      const int r0q = cq * KV_QC;
+      const int qlo = r0q / G, qhi = (min(r0q + KV_QC, p.rows) - 1) / G;
+      int klo, khi;
+      key_range(md, qlo, qhi, klo, khi);
+      const int s0 = max(klo - kb0, 0) >> 4, s1 = (min(khi, kend) - kb0 + 15) >> 4;
+      const bf16* dsb = sm.dS[cq & 1];
+      // two accumulators (even and odd steps), so that consecutive
+      // products do not wait on each other
+      f32x16 acc = {}, acc1 = {};
+      int st = s0;
+      for (; st + 1 < s1; st += 2) {
+        const bf16* kst = sm.K + st * 16 * 64;
+        const bf16* dst_ = dsb + st * 16 * KV_QC;
+        const bf16x8 a = join8(ld_lds_tr4(kst + oK32[0]), ld_lds_tr4(kst + oK32[1]));
+        const bf16x8 bq = join8(ld_lds_tr4(dst_ + oD32[0]), ld_lds_tr4(dst_ + oD32[1]));
+        const bf16x8 a1 = join8(ld_lds_tr4(kst + 16 * 64 + oK32[0]), ld_lds_tr4(kst + 16 * 64 + oK32[1]));
+        const bf16x8 b1 = join8(ld_lds_tr4(dst_ + 16 * KV_QC + oD32[0]), ld_lds_tr4(dst_ + 16 * KV_QC + oD32[1]));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc1, 0, 0, 0);
+      }
+      if (st < s1) {
+        const bf16* kst = sm.K + st * 16 * 64;
+        const bf16* dst_ = dsb + st * 16 * KV_QC;
+        const bf16x8 a = join8(ld_lds_tr4(kst + oK32[0]), ld_lds_tr4(kst + oK32[1]));
+        const bf16x8 bq = join8(ld_lds_tr4(dst_ + oD32[0]), ld_lds_tr4(dst_ + oD32[1]));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
+      }
+      acc += acc1;
+      const int r = r0q + (lane & 31);
+      if (r < p.rows) {
+        const int pos = row_pos(r, p.inv_g);
+        const int hh = r - pos * G;
+        bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + 32 * (wave & 1) + 4 * (lane >> 5);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[4 * q] * p.scale, acc[4 * q + 1] * p.scale, acc[4 * q + 2] * p.scale,
+                           acc[4 * q + 3] * p.scale};
+          *reinterpret_cast<u32x2*>(dst + 8 * q) = __builtin_bit_cast(u32x2, pack4(v));
+        }
+      }
+    }
+  };
   fetch(c_lo);
   stage(sbuf[c_lo & 1]);
   if (c_lo + 1 < nchunks) fetch(c_lo + 1);
@@ -604,7 +689,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     bool anyw = false;
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
-      const int t = wave + KV_W * m;
+      const int t = tile(m);
       const int k0 = kb0 + t * 16, k1 = min(k0 + 16, kend);
       work[m] = t < nkt && !tile_none_visible(md, qlo, qhi, k0, k1);
       if (OP == OP_TIME)
@@ -650,8 +735,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
         f32x4 S[2], dP[2], P[2];
         bf16x8 kop[2];
         if constexpr (KB_LDS) {
-          kop[0] = ld_lds16(sm.K + (wave + KV_W * m) * 16 * 64 + oB[0]);
-          kop[1] = ld_lds16(sm.K + (wave + KV_W * m) * 16 * 64 + oB[1]);
+          kop[0] = ld_lds16(sm.K + tile(m) * 16 * 64 + oB[0]);
+          kop[1] = ld_lds16(sm.K + tile(m) * 16 * 64 + oB[1]);
         } else {
           kop[0] = KB[m][0];
           kop[1] = KB[m][1];
@@ -706,7 +791,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       bf16* dsw = sm.dS[c & 1];
 #pragma unroll
       for (int m = 0; m < TPW; ++m) {
-        const int t = wave + KV_W * m;
+        const int t = tile(m);
         if (t * 16 >= nks) continue;
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
@@ -749,14 +834,16 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     }
     // the previous chunk's dS buffer is complete (written before the last
     // barrier) and is rewritten only after the next one
-    if (FQ && c > c_lo) dq_phase(c - 1);
+    if (DQ32 && c > c_lo) dq_phase32(c - 1);
+    if (FQ && !DQ32 && c > c_lo) dq_phase(c - 1);
     __syncthreads();
   }
-  if (FQ && nchunks > c_lo) dq_phase(nchunks - 1);
+  if (DQ32 && nchunks > c_lo) dq_phase32(nchunks - 1);
+  if (FQ && !DQ32 && nchunks > c_lo) dq_phase(nchunks - 1);
 
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
-    const int key = kb0 + (wave + KV_W * m) * 16 + li;
+    const int key = kb0 + tile(m) * 16 + li;
     if (key >= kend) continue;
     bf16* dkd = p.dk + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;
     bf16* dvd = p.dv + gk.base + (int64_t)key * gk.pos_stride + g * 64 + lg * 4;

@@ -8,6 +8,11 @@
 // use the same one.  The kernels choose that bijection per product so that
 // every operand is one 16-byte LDS or global read.  The output tile holds
 // C[g*4 + j][i], j = 0..3, in the lane's 4 fp32 registers.
+//
+// The dQ step of the three-slot backward uses v_mfma_f32_32x32x16_bf16
+// (32x32 output, 16-deep): lane l holds row l % 32 of A and column l % 32
+// of B for contraction indices 8 (l / 32) .. +7, and output rows
+// 8 (i / 4) + 4 (l / 32) + i % 4 (i < 16) of column l % 32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -19,6 +24,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 

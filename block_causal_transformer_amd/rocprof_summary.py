@@ -199,6 +199,70 @@ def cmd_traffic(args):
     print("\n".join(out))
 
 
+# Counters of the utilisation summary and how each figure is formed (per
+# dispatch, averaged over the dispatches of a kernel).  GRBM_GUI_ACTIVE is
+# the dispatch's duration in GPU clocks; the SQ counters are summed over the
+# 1024 SIMDs (MFMA busy, co-execution) or taken in quad-cycles over the 256
+# CUs (VALU busy), as AMD's derived MfmaUtil, VALUBusy and LDSBankConflict
+# define them.
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU",
+                 "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT",
+                 "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
+SIMDS, CUS, XCDS = 1024, 256, 8
+
+
+def util_figures(c):
+    """Utilisation figures from the per-dispatch averages ``c`` of UTIL_COUNTERS."""
+    # GRBM_GUI_ACTIVE is reported per XCD and summed over the 8: one XCD's
+    # count is the dispatch's duration in clocks
+    gui = c["GRBM_GUI_ACTIVE"] / XCDS
+    return {
+        "mfma_busy_pct": 100.0 * c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS),
+        "coexec_pct": 100.0 * c["SQ_VALU_MFMA_COEXEC_CYCLES"] / (gui * SIMDS),
+        "valu_busy_pct": 100.0 * c["SQ_ACTIVE_INST_VALU"] * 4 / (gui * SIMDS),
+        "lds_bank_conflict_pct": 100.0 * c["SQ_LDS_BANK_CONFLICT"] / (gui * CUS),
+        "lds_active_pct": 100.0 * c["SQ_LDS_IDX_ACTIVE"] / (gui * CUS),
+        "valu_per_mfma": c["SQ_INSTS_VALU"] / max(c["SQ_INSTS_MFMA"], 1.0),
+        "clocks": gui,
+    }
+
+
+def cmd_util(args):
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    names = {}
+    for path in args.csv:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"])
+            if r["Counter_Name"] in UTIL_COUNTERS:
+                per[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                names[k] = op_of(r["Kernel_Name"])
+    out = ["# MFMA / VALU / LDS utilisation per kernel, from rocprofv3 counters", "#",
+           "# command (from the repository root, one MI355X; one counter pass):",
+           "#   " + args.cmd,
+           "# figures per dispatch, averaged over the kernel's dispatches:",
+           "#   mfma_busy_pct  = SQ_VALU_MFMA_BUSY_CYCLES / (clocks * 1024 SIMDs)",
+           "#   coexec_pct     = SQ_VALU_MFMA_COEXEC_CYCLES / (clocks * 1024): MFMA busy while a VALU op issues",
+           "#   valu_busy_pct  = 4 * SQ_ACTIVE_INST_VALU / (clocks * 1024)",
+           "#   lds_*_pct      = SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE / (clocks * 256)",
+           "#   valu_per_mfma  = SQ_INSTS_VALU / SQ_INSTS_MFMA",
+           "#   clocks         = GRBM_GUI_ACTIVE / 8 XCDs (the dispatch's duration in GPU clocks)",
+           "source_files=%s" % ",".join(sorted(args.sources.split(","))),
+           "source_sha=%s" % source_digest(args.sources.split(","))]
+    for k in sorted(per, key=lambda k: (OP_ORDER.index(names[k]) if names[k] in OP_ORDER else 99, k)):
+        c = {n: sum(v) / len(v) for n, v in per[k].items()}
+        if not all(n in c for n in UTIL_COUNTERS):
+            continue
+        f = util_figures(c)
+        op = names[k] or "-"
+        for key, val in f.items():
+            out.append("%s.%s=%.4g  # %s" % (op, key, val, k) if key == "mfma_busy_pct" else
+                       "%s.%s=%.4g" % (op, key, val))
+    out.append("")
+    with open(args.out, "w") as fo:
+        fo.write("\n".join(out))
+    print("\n".join(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -218,9 +282,16 @@ def main(argv=None):
     b.add_argument("--sources", required=True,
                    help="comma-separated csrc/ files the profiled kernels are built from; the "
                         "summary is taken as stale once any of them changes")
+    c = sub.add_parser("util")
+    c.add_argument("out")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--sources", required=True)
     args = ap.parse_args(argv)
     if args.what == "stats":
         cmd_stats(args)
+    elif args.what == "util":
+        cmd_util(args)
     else:
         cmd_traffic(args)
 
