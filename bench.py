@@ -18,7 +18,11 @@ visible (query, key, head) pair forward and 10*D backward; masked and padded
 work is never counted.  Per-op kernel durations come from HIP events on the
 stream the kernels run on.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--spinup-ms 300] [--no-cpu-baseline]
+
+Before the warm-up steps, untimed steps run for ``--spinup-ms`` of wall time
+(the GPU raises its clock over the first tens of milliseconds of work); the
+JSON line reports that phase as ``spinup`` (wall ms and steps).
 
 ``--workload rollout_decode`` instead times one step of frame-by-frame
 generation (section "Artefacts publiés": rollout generation, the demo
@@ -211,6 +215,23 @@ def cpu_baseline_decode(B: int, target_s: float = 12.0):
     }
 
 
+def spin_up(fn, ms):
+    """Call fn() (one untimed step) until at least ms milliseconds have passed.
+
+    The MI355X raises its clock over the first tens of milliseconds of work;
+    a run with a handful of warm-up steps would otherwise time part of that
+    ramp.  Returns {"ms": wall time spent, "steps": calls}."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return {"ms": round((time.perf_counter() - t0) * 1e3, 1), "steps": n}
+
+
 def main_decode(args):
     import torch
     from block_causal_transformer_amd import configs as C, gen, ops
@@ -264,6 +285,7 @@ def main_decode(args):
         space_op(i)
         decode_op(i)
 
+    spin = spin_up(step, args.spinup_ms)
     for i in range(args.warmup):
         step(i % RINGS)
     torch.cuda.synchronize()
@@ -336,6 +358,7 @@ def main_decode(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spinup": spin,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -430,6 +453,12 @@ def main_proj(args):
             raise RuntimeError(ops.bca_last_error())
 
     seq = (("qkv_proj", qkv), ("out_proj", out))
+
+    def one_step():
+        for _, fn in seq:
+            fn()
+
+    spin = spin_up(one_step, args.spinup_ms)
     for _ in range(args.warmup):
         for _, fn in seq:
             fn()
@@ -477,6 +506,7 @@ def main_proj(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spinup": spin,
         "ms_per_step": round(elapsed / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -507,6 +537,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (default: 100; the clock ramps up over the first "
                          "few tens of milliseconds of work)")
+    ap.add_argument("--spinup-ms", type=float, default=300.0,
+                    help="untimed steps for at least this long before the warm-up steps, so that "
+                         "the timed steps run at the GPU's steady clock (reported as spinup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (HBM counter calibration)")
@@ -608,6 +641,11 @@ def main_step(args):
     else:
         labels = {(n, d): "%s_%s_%s" % (n, bufs[n]["w"].op, d) for n, d in seq}
 
+    def one_step():
+        for name, d in seq:
+            call(name, d)
+
+    spin = spin_up(one_step, args.spinup_ms)
     for _ in range(args.warmup):
         for name, d in seq:
             call(name, d)
@@ -686,6 +724,7 @@ def main_step(args):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "spinup": spin,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",

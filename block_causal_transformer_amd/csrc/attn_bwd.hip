@@ -354,6 +354,9 @@ struct KvBuf {
   bf16 dO[KV_QC * 64];
   float lse[KV_QC];     // log2-scaled LSE of the rows (+inf for padding)
   float ndelta[KV_QC];  // -Delta of the rows
+  // space attention: the LSE as agent keys see it, +inf for world rows
+  // (which cannot see them), so that P of such a pair is exp2(-inf) = 0
+  float lse_agent[KV_QC];
 };
 // the lane offsets below add 16 rows as 2048 bytes and reach dO from Q
 static_assert(offsetof(KvBuf, dO) == KV_QC * 64 * 2, "KvBuf layout");
@@ -392,7 +395,10 @@ __device__ __forceinline__ int ds_off(int key, int row) {  // [KMAX][32]
 //
 // Masks are tested on folded row indices r = position * G + head: a key k is
 // visible to row r in time attention iff k*G <= r < (k + W)*G, and a row is
-// an agent row iff agent_begin*G <= r < (agent_begin + agent_count)*G.
+// an agent row iff agent_begin*G <= r < (agent_begin + agent_count)*G.  The
+// space mask (world rows do not see agent keys) costs no per-element test:
+// each chunk carries a second LSE row, +inf for world rows, which the lanes
+// holding agent keys use, so P of a hidden pair is exp2(-inf) = 0 exactly.
 // Keys past the end need no mask: they only feed their own (discarded) dK, dV
 // columns and, with FQ, dQ through K rows that are zero in LDS.
 template <int OP, int TPW, bool FQ>
@@ -434,7 +440,6 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   bf16x8 KB[KB_LDS ? 1 : TPW][2], VB[TPW][2];
   int keyG[TPW];    // time: key * G
   bool kagent[TPW];  // space: the lane's key is an agent key
-  bool keyok[TPW];
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int key = kb0 + tile(m) * 16 + li;
@@ -449,13 +454,19 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     }
     keyG[m] = key * G;
     kagent[m] = (unsigned)(key - p.agent_begin) < (unsigned)p.agent_count;
-    keyok[m] = ok;
   }
   // time: key k is visible to folded row r iff 0 <= r - k*G < winG (no
   // window: the whole sequence, so the test still rejects r < k*G)
   const unsigned winG = (unsigned)((p.window > 0 ? p.window : p.L) * G);
   const int agentG0 = p.agent_begin * G;
   const unsigned agentGn = (unsigned)(p.agent_count * G);
+  // space attention: byte offset in a chunk buffer of the LSE row that this
+  // lane's key of slot m reads; agent keys read the row that is +inf for
+  // world rows, which applies the agent mask with no per-element test
+  int lse_at[TPW];
+#pragma unroll
+  for (int m = 0; m < TPW; ++m)
+    lse_at[m] = (int)(kagent[m] ? offsetof(KvBuf, lse_agent) : offsetof(KvBuf, lse));
 
   f32x4 dKT[TPW][4], dVT[TPW][4];
 #pragma unroll
@@ -477,13 +488,14 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const int srow = (tid & 255) >> 3, sch = tid & 7;
   bf16x8 pre = zero8(), pre_o = zero8();
   float pre_s = 0.f;
-  bool pre_valid = false;
+  bool pre_valid = false, pre_agent = false;
   int64_t pre_lo = 0;
   auto fetch = [&](int c) {
     if (KV_W > 8 && !stager) return;
     // padding rows read a real (clamped) row; their LSE of +inf zeroes P
     const int r = c * KV_QC + srow;
     pre_valid = r < p.rows;
+    if constexpr (OP == OP_SPACE) pre_agent = (unsigned)(r - agentG0) < agentGn;
     const int rr = min(r, p.rows - 1);
     const int pos = row_pos(rr, p.inv_g);
     const int hh = rr - pos * G;
@@ -504,7 +516,11 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     if (KV_W > 8 && !stager) return;
     st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
     if (carries_q) {
-      if (sch == 0) b.lse[srow] = pre_valid ? pre_s * kLog2e : INFINITY;
+      if (sch == 0) {
+        const float l2 = pre_valid ? pre_s * kLog2e : INFINITY;
+        b.lse[srow] = l2;
+        if constexpr (OP == OP_SPACE) b.lse_agent[srow] = pre_agent ? l2 : INFINITY;
+      }
     } else {
       float t = 0.f;
 #pragma unroll
@@ -684,7 +700,6 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     const int r0 = c * KV_QC;
     const int qlo = r0 / G;
     const int qhi = (min(r0 + KV_QC, p.rows) - 1) / G;
-    const bool world_rows = !(qlo >= p.agent_begin && qhi < p.agent_begin + p.agent_count);
     bool work[TPW], edge[TPW];
     bool anyw = false;
 #pragma unroll
@@ -692,10 +707,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       const int t = tile(m);
       const int k0 = kb0 + t * 16, k1 = min(k0 + 16, kend);
       work[m] = t < nkt && !tile_none_visible(md, qlo, qhi, k0, k1);
-      if (OP == OP_TIME)
-        edge[m] = !tile_all_visible(md, qlo, qhi, k0, k1);
-      else
-        edge[m] = world_rows && p.agent_count > 0 && k0 < p.agent_begin + p.agent_count && k1 > p.agent_begin;
+      // (space attention needs no per-element mask: see lse_at)
+      edge[m] = OP == OP_TIME && !tile_all_visible(md, qlo, qhi, k0, k1);
       anyw |= work[m];
     }
     bf16x8 Pb[TPW], dSb[TPW];
@@ -706,10 +719,13 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       bf16x4 Ph[TPW][2], dSh[TPW][2];
       bf16x8 Qa[2][2], dOa[2][2];
       f32x4 lse4[2], ndl4[2];
-      auto load_stats = [&]() {
+      auto load_stats = [&](int m) {
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-          lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
+          if constexpr (OP == OP_SPACE)
+            lse4[qt] = *reinterpret_cast<const f32x4*>(bb + lse_at[m] + (qt * 16 + lg * 4) * 4);
+          else
+            lse4[qt] = *reinterpret_cast<const f32x4*>(b.lse + qt * 16 + lg * 4);
           ndl4[qt] = *reinterpret_cast<const f32x4*>(b.ndelta + qt * 16 + lg * 4);
         }
       };
@@ -721,16 +737,18 @@ void attn_bwd_dkv_kernel(BwdParams p) {
           dOa[qt][s] = ld_lds16(reinterpret_cast<const bf16*>(bb + offQ[s] + qt * 2048 + KV_QC * 128));
         }
       }
-      if constexpr (TPW < 3) load_stats();
+      // one read of the statistics per chunk, or per slot: with three slots
+      // (register pressure) and for space attention (each slot's LSE row)
+      constexpr bool STATS_PER_TILE = TPW >= 3 || OP == OP_SPACE;
+      if constexpr (!STATS_PER_TILE) load_stats(0);
       const int rb = r0 + lg * 4;  // folded row of element j of half qt: rb + 16 qt + j
 #pragma unroll
       for (int m = 0; m < TPW; ++m) {
         if (!work[m]) continue;
-        if constexpr (TPW >= 3) {
-          // with three tiles the row statistics are read again for every
-          // tile rather than held across the loop (register pressure)
+        if constexpr (STATS_PER_TILE) {
+          // read again for every slot rather than held across the loop
           asm volatile("" ::: "memory");
-          load_stats();
+          load_stats(m);
         }
         f32x4 S[2], dP[2], P[2];
         bf16x8 kop[2];
@@ -762,11 +780,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
           for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              bool vis;
-              if (OP == OP_TIME)
-                vis = (unsigned)(rb + qt * 16 + j - keyG[m]) < winG;
-              else
-                vis = keyok[m] && (!kagent[m] || (unsigned)(rb + qt * 16 + j - agentG0) < agentGn);
+              const bool vis = (unsigned)(rb + qt * 16 + j - keyG[m]) < winG;
               P[qt][j] = vis ? P[qt][j] : 0.f;
             }
         }
