@@ -481,17 +481,20 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   // otherwise): the first 256 staging threads carry Q (and LSE), the next 256
   // dO (and Delta); a piece is (row, 16-byte column chunk) of the chunk.  The
   // loads are only issued by fetch(); the LSE transform waits for stage() so
-  // that no wave stalls on a global load a chunk early.
+  // that no wave stalls on a global load a chunk early.  In the DQ32 layout
+  // waves 0..3 stage both halves (each thread its Q and its dO piece), so
+  // that the dQ waves 6, 7 stage nothing.
+  constexpr bool STAGE_LOW = DQ32;
   const int stid = KV_W > 8 ? tid - 512 : tid;
   const bool carries_q = (stid & 511) < 256;
-  const bool stager = stid >= 0;
+  const bool stager = KV_W > 8 ? stid >= 0 : !STAGE_LOW || tid < 256;
   const int srow = (tid & 255) >> 3, sch = tid & 7;
-  bf16x8 pre = zero8(), pre_o = zero8();
+  bf16x8 pre = zero8(), pre_o = zero8(), pre_q = zero8();
   float pre_s = 0.f;
   bool pre_valid = false, pre_agent = false;
   int64_t pre_lo = 0;
   auto fetch = [&](int c) {
-    if (KV_W > 8 && !stager) return;
+    if (!stager) return;
     // padding rows read a real (clamped) row; their LSE of +inf zeroes P
     const int r = c * KV_QC + srow;
     pre_valid = r < p.rows;
@@ -501,11 +504,18 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     const int hh = rr - pos * G;
     const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + sch * 8;
     const int64_t lo = gl.base + (int64_t)pos * gl.pos_stride + g * G + hh;
-    pre = ld_global16((carries_q ? p.q : p.dout) + off);
-    if (carries_q)
+    if constexpr (STAGE_LOW) {
+      pre_q = ld_global16(p.q + off);
       pre_s = p.lse[lo];
-    else
+      pre = ld_global16(p.dout + off);
       pre_o = ld_global16(p.o + off);
+    } else {
+      pre = ld_global16((carries_q ? p.q : p.dout) + off);
+      if (carries_q)
+        pre_s = p.lse[lo];
+      else
+        pre_o = ld_global16(p.o + off);
+    }
     pre_lo = lo;
   };
   // Delta = rowsum(dO * O) is formed here, from the 8 pieces of a row held by
@@ -513,15 +523,21 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   // goes to the workspace for the dq kernel (which runs after this one), where
   // workgroups whose chunk ranges overlap write the same bits
   auto stage = [&](KvBuf& b) {
-    if (KV_W > 8 && !stager) return;
-    st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
-    if (carries_q) {
+    if (!stager) return;
+    if constexpr (STAGE_LOW) {
+      st_lds16(b.Q + row_off(srow, sch), pre_q);
+      st_lds16(b.dO + row_off(srow, sch), pre);
+    } else {
+      st_lds16((carries_q ? b.Q : b.dO) + row_off(srow, sch), pre);
+    }
+    if (STAGE_LOW || carries_q) {
       if (sch == 0) {
         const float l2 = pre_valid ? pre_s * kLog2e : INFINITY;
         b.lse[srow] = l2;
         if constexpr (OP == OP_SPACE) b.lse_agent[srow] = pre_agent ? l2 : INFINITY;
       }
-    } else {
+    }
+    if (STAGE_LOW || !carries_q) {
       float t = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) t = __builtin_fmaf((float)pre[e], (float)pre_o[e], t);
@@ -689,6 +705,13 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       }
     }
   };
+  // DQ32: the waves that stage nothing (4..7) issue first on their SIMD, so
+  // that the two waves of a SIMD (w, w + 4) reach the chunk barrier closer
+  // together (measured per-wave: the older wave 0..3 otherwise ran ahead
+  // and waited at the barrier while its partner finished alone)
+  if constexpr (DQ32) {
+    if (wave >= 4) __builtin_amdgcn_s_setprio(1);
+  }
   fetch(c_lo);
   stage(sbuf[c_lo & 1]);
   if (c_lo + 1 < nchunks) fetch(c_lo + 1);
