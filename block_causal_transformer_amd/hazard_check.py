@@ -62,7 +62,9 @@ def _parse(lines):
 
 
 def _kernels(text: str):
-    """(name, lines) of every function body in an assembly file."""
+    """(name, lines) of every function body in an assembly file: from the
+    function's label to its end marker (.Lfunc_endN), so that code after an
+    early s_endpgm (a returning path) is checked too."""
     out, name, cur = [], None, []
     for ln in text.split("\n"):
         m = re.match(r"^([A-Za-z_][\w.$]*):", ln)
@@ -70,10 +72,13 @@ def _kernels(text: str):
             name, cur = m.group(1), []
             continue
         if name is not None:
-            cur.append(ln)
-            if "s_endpgm" in ln:
+            if re.match(r"^\.Lfunc_end\d+:", ln):
                 out.append((name, cur))
                 name = None
+                continue
+            cur.append(ln)
+    if name is not None:
+        out.append((name, cur))
     return out
 
 
@@ -116,11 +121,12 @@ def check_function(lines, min_states=None):
             nst = st + (int(a2[0], 0) + 1 if op2 == "s_nop" else 1)
             if op2 == "s_endpgm":
                 continue
-            if op2 == "s_branch":
+            if op2 == "s_branch" or op2.startswith("s_cbranch"):
+                if a2[0] not in labels:
+                    raise ValueError("branch to %s, which is not in the function" % a2[0])
                 stack.append((labels[a2[0]], nst))
-                continue
-            if op2.startswith("s_cbranch"):
-                stack.append((labels[a2[0]], nst))
+                if op2 == "s_branch":
+                    continue
             stack.append((j + 1, nst))
     return bad
 

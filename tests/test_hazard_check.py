@@ -92,3 +92,25 @@ def test_unknown_mfma_opcode_fails():
 """
     bad = H.check_text(text)
     assert "k" in bad and "unknown MFMA" in bad["k"][0][1]
+
+
+def test_code_after_an_early_endpgm_is_checked():
+    # a kernel with a returning path: the body runs to the function's end
+    # marker, not to its first s_endpgm
+    text = """k:
+\ts_cbranch_scc1 .LBB0_3
+\ts_endpgm
+.LBB0_3:
+\tv_mfma_f32_16x16x32_bf16 v[4:7], v[0:3], v[8:11], v[4:7]
+\tv_mul_f32_e32 v4, v12, v4
+\ts_endpgm
+.Lfunc_end0:
+"""
+    bad = H.check_text(text)
+    assert "k" in bad and "v_mul_f32" in bad["k"][0][1], bad
+
+
+def test_branch_out_of_the_function_is_an_error():
+    with pytest.raises(ValueError):
+        H.check_text("k:\n\tv_mfma_f32_16x16x32_bf16 v[4:7], v[0:3], v[8:11], v[4:7]\n"
+                     "\ts_branch .LBB9_1\n\ts_endpgm\n.Lfunc_end0:\n")
