@@ -47,7 +47,9 @@
 // that the causal / window ranges make invisible are never visited.  For
 // long problems the split costs two more matmul passes (S and dP are formed
 // in both kernels) in exchange for no cross-workgroup sum of dQ.
+#include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "bca_device.h"
 #include "bca_kernels.h"
@@ -75,6 +77,12 @@ struct BwdParams {
   int splits, rows_per_split;  // dq kernel
   int kvb, kbl;                // dkv kernel: key blocks per problem, keys per block
   int poison;                  // debug: NaN-fill LDS before staging
+  // fused backward, last round split: problems from split_base on run as
+  // two workgroups each, rows of chunks [.., split_chunk) and [split_chunk,
+  // ..), whose fp32 dK, dV partials (split_keys keys x 128 per half) go to
+  // part and are summed by the reduce kernel
+  int split_base, split_chunk, split_keys;
+  float* part;
 };
 
 // ------------------------------------------------------------- dq kernel
@@ -413,9 +421,17 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     __syncthreads();
   }
 
-  // workgroup = (problem, block of kbl keys); one block for L <= 320
-  int ug, kb;
-  xcd_remap(blockIdx.x, p.units * p.Hkv, p.kvb, ug, kb);
+  // workgroup = (problem, block of kbl keys); one block for L <= 320.  With
+  // FQ, workgroups from split_base on are halves of the last problems.
+  int ug, kb, half = -1;
+  if (FQ && (int)blockIdx.x >= p.split_base) {
+    const int j = (int)blockIdx.x - p.split_base;
+    ug = p.split_base + (j >> 1);
+    half = j & 1;
+    kb = 0;
+  } else {
+    xcd_remap(blockIdx.x, p.units * p.Hkv, p.kvb, ug, kb);
+  }
   const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
   const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, 64);
   const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
@@ -563,6 +579,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       c_hi = min(c_hi, (int)((rend + KV_QC - 1) / KV_QC));
     }
   }
+  if (half == 0) c_hi = min(c_hi, p.split_chunk);
+  if (half == 1) c_lo = max(c_lo, p.split_chunk);
   const int nchunks = c_hi;
 
   // byte offsets of this lane's LDS reads within a chunk buffer, formed once
@@ -878,6 +896,21 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   if (DQ32 && nchunks > c_lo) dq_phase32(nchunks - 1);
   if (FQ && !DQ32 && nchunks > c_lo) dq_phase(nchunks - 1);
 
+  if (FQ && half >= 0) {
+    // a half problem: its fp32 partials, keys x (64 dK, 64 dV)
+    float* dst = p.part + ((int64_t)(ug - p.split_base) * 2 + half) * p.split_keys * 128;
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int key = kb0 + tile(m) * 16 + li;
+      if (key >= kend) continue;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        *reinterpret_cast<f32x4*>(dst + (int64_t)key * 128 + dt * 16 + lg * 4) = dKT[m][dt];
+        *reinterpret_cast<f32x4*>(dst + (int64_t)key * 128 + 64 + dt * 16 + lg * 4) = dVT[m][dt];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int key = kb0 + tile(m) * 16 + li;
@@ -892,7 +925,99 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   }
 }
 
+// dK, dV of the split problems: the two halves' fp32 partials summed in a
+// fixed order (half 0 + half 1), scaled (dK) and rounded to bf16.  One thread
+// per (split problem, key, 8 head dims of dK or of dV).
+template <int OP>
+__global__ __launch_bounds__(256) void attn_bwd_split_reduce_kernel(BwdParams p, int count) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = (int64_t)p.L * 16;
+  if (idx >= (int64_t)count * per) return;
+  const int sp = (int)(idx / per);
+  const int rem = (int)(idx - (int64_t)sp * per);
+  const int key = rem >> 4, pc = rem & 15;
+  const int ug = p.split_base + sp;
+  const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
+  const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
+  const float* a = p.part + ((int64_t)sp * 2 * p.split_keys + key) * 128 + pc * 8;
+  const float* b = a + (int64_t)p.split_keys * 128;
+  const float sc = pc < 8 ? p.scale : 1.0f;
+  const f32x4 a0 = *reinterpret_cast<const f32x4*>(a), a1 = *reinterpret_cast<const f32x4*>(a + 4);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
+  bf16* dst = (pc < 8 ? p.dk : p.dv) + gk.base + (int64_t)key * gk.pos_stride + g * 64 + (pc & 7) * 8;
+  st_global16(dst, pack8((a0 + b0) * sc, (a1 + b1) * sc));
+}
+
+// Number of compute units of the current device (0 if none).
+int device_cu_count() {
+  int dev = -1, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+// The fused backward runs one workgroup per problem, one per CU, so the
+// problems go through the device in rounds of `cus`.  When the last round
+// is at most half full, its problems are split in two by rows, so that it
+// takes about half as long.  The split chunk balances an estimate of the
+// chunks' cost: a fixed part and one part per key tile a chunk sees, 28 to
+// 1 (timed per chunk: ~2900 cycles with one visible tile, ~4150 with 13).
+struct SplitPlan {
+  int base = 0x7fffffff, count = 0, chunk = 0, keys = 0;
+};
+
+SplitPlan plan_split(const AttnDims& d) {
+  SplitPlan sp;
+  if (!bwd_uses_mfma(d) || uses_short(d) || attended_length(d) > kBwdKeyBlock) return sp;
+  const int cus = device_cu_count();
+  const long problems = (long)(d.op == OP_SPACE ? d.B * d.T : d.B * d.N) * d.Hkv;
+  if (cus <= 0 || problems <= cus) return sp;
+  const long tail = problems % cus;
+  if (tail == 0 || tail > cus / 2) return sp;
+  const int G = d.Hq / d.Hkv, L = attended_length(d);
+  const long rows = (long)L * G;
+  const int chunks = (int)((rows + KV_QC - 1) / KV_QC);
+  const int nkt = (L + 15) / 16;
+  if (chunks < 2) return sp;
+  std::vector<long> cost(chunks);
+  long total = 0;
+  for (int c = 0; c < chunks; ++c) {
+    const int qlo = (int)((long)c * KV_QC / G);
+    const int qhi = (int)((std::min<long>((long)c * KV_QC + KV_QC, rows) - 1) / G);
+    int seen = 0;
+    for (int t = 0; t < nkt; ++t) {
+      const int k0 = t * 16, k1 = std::min(k0 + 16, L);
+      bool none = false;
+      if (d.op == OP_TIME) none = k0 > qhi || (d.window > 0 && qlo - (k1 - 1) >= d.window);
+      seen += none ? 0 : 1;
+    }
+    cost[c] = 28 + seen;
+    total += cost[c];
+  }
+  long acc = 0;
+  int best = 1;
+  long best_gap = -1;
+  for (int c = 1; c < chunks; ++c) {
+    acc += cost[c - 1];
+    const long gap = std::max(acc, total - acc);
+    if (best_gap < 0 || gap < best_gap) {
+      best_gap = gap;
+      best = c;
+    }
+  }
+  sp.base = (int)(problems - tail);
+  sp.count = (int)tail;
+  sp.chunk = best;
+  sp.keys = nkt * 16;
+  return sp;
+}
+
 }  // namespace
+
+size_t bwd_split_bytes(const AttnDims& d) {
+  const SplitPlan sp = plan_split(d);
+  return (size_t)sp.count * 2 * sp.keys * 128 * sizeof(float);
+}
 
 size_t bwd_bf16_workspace_bytes(const AttnDims& d) {
   return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
@@ -981,7 +1106,15 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   // blocks of equal size in whole tiles
   p.kvb = (p.L + KMAX - 1) / KMAX;
   p.kbl = (((p.L + p.kvb - 1) / p.kvb) + 15) & ~15;
-  const long g2 = problems * p.kvb;
+  // one key block: the last round's problems may run as two halves each,
+  // their dK, dV partials in the workspace (sized by bwd_split_bytes)
+  const SplitPlan sp = p.kvb == 1 ? plan_split(d) : SplitPlan{};
+  p.split_base = sp.base;
+  p.split_chunk = sp.chunk;
+  p.split_keys = sp.keys;
+  p.part = static_cast<float*>(workspace);
+  if (sp.count > 0 && !workspace) return hipErrorInvalidValue;
+  const long g2 = problems * p.kvb + sp.count;
   if (g1 > 0x7fffffff || g2 > 0x7fffffff) return hipErrorInvalidValue;
 
   // Waves and tile slots per key block (measured): the fused time backward
@@ -1004,6 +1137,9 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
     else
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, false>), g2d, b8, 0, stream, p);
     if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_SPACE>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
+    if (sp.count > 0)
+      hipLaunchKernelGGL(attn_bwd_split_reduce_kernel<OP_SPACE>, dim3((unsigned)((sp.count * (long)p.L * 16 + 255) / 256)),
+                         dim3(256), 0, stream, p, sp.count);
   } else {
     if (tpw == 1)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true>), g2d, bw, 0, stream, p);
@@ -1014,6 +1150,9 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
     else
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, false>), g2d, b8, 0, stream, p);
     if (!fq) hipLaunchKernelGGL(attn_bwd_dq_kernel<OP_TIME>, dim3((unsigned)g1), dim3(DQ_W * 64), 0, stream, p);
+    if (sp.count > 0)
+      hipLaunchKernelGGL(attn_bwd_split_reduce_kernel<OP_TIME>, dim3((unsigned)((sp.count * (long)p.L * 16 + 255) / 256)),
+                         dim3(256), 0, stream, p, sp.count);
   }
   return hipGetLastError();
 }

@@ -93,7 +93,8 @@ int check_ptrs(const char* const* names, const void* const* ptrs, int n) {
 }
 
 size_t workspace_bytes(const bca::AttnDims& d) {
-  if (!bca::bwd_needs_workspace(d)) return 0;
+  if (bca::uses_short(d)) return 0;
+  if (!bca::bwd_needs_workspace(d)) return bca::bwd_uses_mfma(d) ? bca::bwd_split_bytes(d) : 0;
   if (bca::bwd_uses_mfma(d)) return bca::bwd_bf16_workspace_bytes(d);
   return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
 }

@@ -65,9 +65,16 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
 // (query, head), written by its first kernel and read by its second.
 size_t bwd_bf16_workspace_bytes(const AttnDims& d);
 
+// Workspace of the fused MFMA backward (one key block per problem) on the
+// current device: when its problems fill the CUs in rounds and the last
+// round is at most half full, that round's problems run as two workgroups
+// each (split by rows) whose fp32 dK, dV partials (2 x keys x 128 floats
+// per problem) go here; 0 when nothing is split (or there is no device).
+size_t bwd_split_bytes(const AttnDims& d);
+
 // Size of the static device scratch of the no-allocation backward (the
-// Delta workspace, one fp32 per (query, head)): 64 MiB, i.e. up to 2^24
-// (query, head) rows per call.
+// Delta workspace, one fp32 per (query, head), or the split partials above):
+// 64 MiB, i.e. up to 2^24 (query, head) rows per call.
 constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 // Device address of that scratch on the current device (looked up once per
 // device with hipGetSymbolAddress and kept); allocates nothing.
@@ -126,7 +133,8 @@ constexpr long kMaxFoldedRows = 1L << 21;
 
 // True when the backward needs the Delta workspace: the MFMA path whose
 // problems span more than one key block (dQ then comes from a second
-// kernel that reads Delta), and the generic VALU path.
+// kernel that reads Delta), and the generic VALU path.  (The fused MFMA
+// path may still take a workspace for split problems: bwd_split_bytes.)
 inline bool bwd_needs_workspace(const AttnDims& d) {
   if (uses_short(d)) return false;
   if (bwd_uses_mfma(d)) return attended_length(d) > kBwdKeyBlock;

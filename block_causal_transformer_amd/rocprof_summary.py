@@ -38,6 +38,8 @@ OPS = [
     (r"attn_bwd_dkv_kernel<0[,>]", "space_bwd"),
     (r"attn_bwd_dq_kernel<1[,>]", "time_bwd"),
     (r"attn_bwd_dkv_kernel<1[,>]", "time_bwd"),
+    (r"attn_bwd_split_reduce_kernel<0>", "space_bwd"),
+    (r"attn_bwd_split_reduce_kernel<1>", "time_bwd"),
     (r"rmsnorm_rows_kernel", "qkv_proj"),
     (r"gemm256_kernel<0[,>]", "qkv_proj"),
     (r"gemm_nt_kernel<0>", "qkv_proj"),
@@ -248,12 +250,22 @@ def cmd_util(args):
            "#   clocks         = GRBM_GUI_ACTIVE / 8 XCDs (the dispatch's duration in GPU clocks)",
            "source_files=%s" % ",".join(sorted(args.sources.split(","))),
            "source_sha=%s" % source_digest(args.sources.split(","))]
+    # an op with several kernels (the split backward's reduce) is keyed by
+    # its longest kernel; the others by op/kernel
+    clocks = {k: sum(per[k]["GRBM_GUI_ACTIVE"]) / max(len(per[k]["GRBM_GUI_ACTIVE"]), 1) for k in per}
+    main_of = {}
+    for k in per:
+        op = names[k]
+        if op and (op not in main_of or clocks[k] > clocks[main_of[op]]):
+            main_of[op] = k
     for k in sorted(per, key=lambda k: (OP_ORDER.index(names[k]) if names[k] in OP_ORDER else 99, k)):
         c = {n: sum(v) / len(v) for n, v in per[k].items()}
         if not all(n in c for n in UTIL_COUNTERS):
             continue
         f = util_figures(c)
         op = names[k] or "-"
+        if names[k] and main_of.get(names[k]) != k:
+            op = "%s/%s" % (op, k.split("<")[0])
         for key, val in f.items():
             out.append("%s.%s=%.4g  # %s" % (op, key, val, k) if key == "mfma_busy_pct" else
                        "%s.%s=%.4g" % (op, key, val))

@@ -179,7 +179,8 @@ int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const voi
  * taken from a static device array of the library instead of an argument.
  * It calls no hipMalloc, hipFree or allocating library routine.  The array
  * holds 64 MiB per GPU (kept until the process ends), enough for
- * B*T*N*Hq <= 2^24 (query, head) rows; shapes that need more workspace
+ * B*T*N*Hq <= 2^24 (query, head) rows or the split partials of up to 128
+ * problems; shapes that need more workspace
  * (bca_bwd_workspace_bytes(BCA_OP_TIME, shape) > 64 MiB) are refused with
  * BCA_ERR_INVALID_ARG before any launch.  Every call on one GPU uses that
  * GPU's one array: calls that overlap in time on one GPU (other streams,
@@ -191,13 +192,20 @@ int time_attn_bwd_noalloc(const bca_shape* shape, const bca_mask* mask, const vo
                           const void* dout, void* dq, void* dk, void* dv, void* stream);
 
 /* Bytes of device workspace the backward of `op` (BCA_OP_SPACE or
- * BCA_OP_TIME) needs for `shape`: 0 when the attended length (N for space, T
- * for time) is at most 320 on the bf16 head_dim-64 path (every problem is one
- * key block and one kernel forms dQ, dK and dV), else one fp32
- * Delta = rowsum(dO * O) per (query, head), B*T*N*Hq*4 bytes, which the
- * backward's first kernel writes and its second reads.  The op is an
- * argument because the attended length depends on it.  Returns 0 for an
- * invalid shape or op. */
+ * BCA_OP_TIME) needs for `shape` on the current device.  On the bf16
+ * head_dim-64 path with an attended length (N for space, T for time) of at
+ * most 320, every problem (a block or slot and a KV head) is one key block
+ * and one kernel forms dQ, dK and dV; it runs one workgroup per problem and
+ * compute unit, so the problems pass through the device in rounds.  When
+ * there are more problems than compute units and the last round is at most
+ * half full, that round's problems each run as two workgroups (one per half
+ * of the query rows), whose fp32 dK, dV partials, 2 * ceil(L/16)*16 * 128 * 4
+ * bytes per such problem, go to the workspace and are summed in a fixed
+ * order by a second kernel; otherwise this path needs 0 bytes.  With longer
+ * attended lengths the backward needs one fp32 Delta = rowsum(dO * O) per
+ * (query, head), B*T*N*Hq*4 bytes, which its first kernel writes and its
+ * second reads.  The op is an argument because the attended length depends
+ * on it.  Returns 0 for an invalid shape or op. */
 size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape);
 
 /* ---- projections beside attention ----

@@ -42,6 +42,7 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void*, const void*, con
   return rec(d);
 }
 size_t bwd_bf16_workspace_bytes(const AttnDims& d) { return (size_t)d.B * d.T * d.N * d.Hq * 4; }
+size_t bwd_split_bytes(const AttnDims&) { return 0; }  // no device in this build
 hipError_t launch_attn_fwd_generic(const AttnDims& d, const void*, const void*, const void*, void*, float*,
                                    hipStream_t) { return rec(d); }
 hipError_t launch_attn_bwd_generic(const AttnDims& d, const void*, const void*, const void*, const void*,

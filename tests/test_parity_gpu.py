@@ -143,6 +143,21 @@ RAGGED += [
     C.Workload("mfma_space_N33", "space", 1, 2, 33, 6, 2, 64, "bf16", 0, 32, 1, 1.0, 9026),
     C.Workload("mfma_time_T33_W8", "time", 1, 33, 2, 2, 2, 64, "bf16", 8, 0, 0, 1.0, 9027),
 ]
+# More problems than CUs with a last round at most half full: the fused
+# backward runs that round's problems as two row halves each and sums their
+# dK, dV partials (one case per fused instance; 256 CUs on the MI355X).  The
+# time case with config 4's slots draws dO at quarter scale: at unit scale
+# its dK sits on the same precision floor as config 4's whole-tensor test
+# (one bf16 step at |dK| ~ 8 from the method's bf16 operand roundings
+# alone), which that test covers with the stored floor.
+SPLIT = [
+    C.Workload("split_space_P300_N74", "space", 1, 100, 74, 6, 3, 64, "bf16", 0, 73, 1, 1.0, 9030),
+    C.Workload("split_space_P258_N290", "space", 1, 86, 290, 30, 3, 64, "bf16", 0, 289, 1, 1.0, 9031),
+    C.Workload("split_time_P300_T256", "time", 1, 256, 100, 30, 3, 64, "bf16", 192, 0, 0, 1.0, 9032,
+               dout_scale=0.25),
+    C.Workload("split_time_P300_T300", "time", 1, 300, 100, 6, 3, 64, "bf16", 192, 0, 0, 1.0, 9033),
+]
+RAGGED += SPLIT
 
 
 @pytest.mark.parametrize("w", RAGGED, ids=[w.name for w in RAGGED])
@@ -153,6 +168,22 @@ def test_parity_ragged(w):
     got = U.run_hip(w, inp)
     want = U.run_oracle(w, inp)
     print(U.assert_close(w, got, want, w.name))
+
+
+def test_split_cases_split():
+    """The split cases above do split on this device (their workspace holds
+    the halves' partials), so their parity tests cover the split path."""
+    _needs_gpu()
+    import torch
+    from block_causal_transformer_amd import ops
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the split cases are sized for 256 CUs")
+    for w in SPLIT:
+        opc = ops.BCA_OP_SPACE if w.op == "space" else ops.BCA_OP_TIME
+        shape = ops.BcaShape(w.B, w.T, w.N, w.Hq, w.Hkv, w.D, 0)
+        problems = (w.B * w.T if w.op == "space" else w.B * w.N) * w.Hkv
+        keys = ((w.N if w.op == "space" else w.T) + 15) // 16 * 16
+        assert ops.bca_bwd_workspace_bytes(opc, shape) == (problems - 256) * 2 * keys * 128 * 4, w.name
 
 
 def test_parity_custom_scale():
