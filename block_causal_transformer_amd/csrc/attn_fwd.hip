@@ -55,6 +55,7 @@ struct FwdParams {
   int T, N, Hq, Hkv, G, L, units, rows;
   int window, agent_begin, agent_count;
   float scale_log2, inv_g;
+  float inv_scale_log2;  // 1 / scale_log2
   int splits, rows_per_split;
   // decode: K/V hold Tk frames per slot; kernel key position x is absolute
   // frame kfirst + x at frame (kfirst + x) % Tk; kernel query position y sits
@@ -309,7 +310,11 @@ void attn_fwd_kernel(FwdParams p) {
             for (int dt = 0; dt < 4; ++dt) acc[qt][dt] *= alpha;
             m[qt] = mn;
             negm[qt] = (mn == -INFINITY) ? 0.f : -mn;
-            thr[qt] = (mn + kRescaleThreshold) / p.scale_log2;
+            // (the bound only decides when the test above runs; an ulp
+            // either way can change whether a score right at the threshold
+            // moves the reference, which the results do not depend on
+            // beyond rounding)
+            thr[qt] = (mn + kRescaleThreshold) * p.inv_scale_log2;
           }
         }
         bf16x8 pb[NQ];
@@ -344,7 +349,7 @@ void attn_fwd_kernel(FwdParams p) {
       for (int qt = 0; qt < NQ; ++qt) {
         const float lt = group4_sum(l[qt]);
         if (!qvalid[qt]) continue;
-        const float inv = 1.f / lt;
+        const float inv = __builtin_amdgcn_rcpf(lt);  // (O is rounded to bf16)
         bf16* dst = obase + qpos[qt] * gq.pos_stride + hh[qt] * 64 + lg * 4;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
@@ -391,6 +396,7 @@ hipError_t launch_attn_fwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.agent_begin = d.agent_begin;
   p.agent_count = d.agent_count;
   p.scale_log2 = d.scale * kLog2e;
+  p.inv_scale_log2 = 1.0f / p.scale_log2;
   p.inv_g = 1.0f / (float)p.G;
   p.poison = d.poison;
   if (p.G > 256 || (long)p.rows >= (1L << 21)) return hipErrorInvalidValue;
