@@ -1,8 +1,9 @@
 """time_attn_bwd_noalloc (the backward whose workspace is the library's static
 device scratch) against time_attn_bwd with a caller-allocated workspace,
 through the C ABI: two calls in a row, the second with a smaller input, both
-needing the scratch (more than 320 frames: the Delta workspace is used), plus
-a shape that needs none and one the scratch cannot hold.  Same kernels, so the
+needing the scratch (more than 320 frames: the Delta workspace is used), a
+shape whose split last round puts its partials there, plus a shape that
+needs none and one the scratch cannot hold.  Same kernels, so the
 results must be bitwise equal; the first call is also checked against the
 oracle."""
 import numpy as np
@@ -53,6 +54,22 @@ def test_noalloc_matches_allocating_backward_twice():
             want = U.run_oracle(w, inp)
             print(U.assert_close(w, {"dq": U.to_np(got[0]), "dk": U.to_np(got[1]), "dv": U.to_np(got[2])},
                                  want, w.name + " noalloc"))
+
+
+def test_noalloc_split_last_round():
+    """A fused-path shape whose last round of problems is split (300 problems
+    on 256 CUs): the halves' dK, dV partials go to the static scratch."""
+    _needs_gpu()
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("sized for 256 CUs")
+    w = C.Workload("time_T256_N100_split", "time", 1, 256, 100, 30, 3, 64, "bf16", 192, 0, 0, 1.0, 9303,
+                   dout_scale=0.25)
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, ops.BcaShape(1, 256, 100, 30, 3, 64, 0)) > 0
+    inp = gen.make_inputs(w)
+    ref, got = _both(w, inp)
+    for name, a, b in zip(("dq", "dk", "dv"), ref, got):
+        assert torch.equal(a, b), "%s differs from time_attn_bwd" % name
 
 
 def test_noalloc_without_workspace_and_oversize():
