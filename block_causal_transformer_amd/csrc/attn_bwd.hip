@@ -16,7 +16,8 @@
 // with dK, dV of a KV head summed over the G query heads of its group.
 //
 // Two kernels, each keeping one side of the problem stationary in registers
-// so that no sum crosses waves (no atomics; bitwise deterministic):
+// so that no sum crosses waves (no atomics; bitwise deterministic; the split
+// last round above adds its two halves in a fixed order):
 //
 //  dkv kernel (key-parallel, launched first): each wave owns 16-key tiles
 //             of one problem and keeps their dK^T, dV^T accumulators and K, V
@@ -34,7 +35,14 @@
 //             256 keys (three tile slots), by two dedicated waves as two
 //             32 x 32 blocks on v_mfma_f32_32x32x16_bf16 (half the operand
 //             reads per product), those two waves keeping one key tile each.
-//             The dq kernel is then not launched.
+//             The dq kernel is then not launched.  In that three-slot
+//             layout waves 0..3 stage whole chunks and waves 4..7 run at
+//             wave priority 1, so both waves of a SIMD reach the chunk
+//             barrier together.  One workgroup per problem and CU makes the
+//             problems pass through the device in rounds; a last round at
+//             most half full runs as two workgroups per problem (query rows
+//             split), whose fp32 dK, dV partials a small kernel sums in a
+//             fixed order.
 //  dq kernel  (query-parallel, laid out like the forward; longer problems
 //             only): a workgroup holds K, V and K^T of one (unit, KV head)
 //             problem's key block in LDS; each wave owns 32 query rows
