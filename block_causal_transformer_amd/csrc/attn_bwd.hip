@@ -716,6 +716,11 @@ void attn_bwd_dkv_kernel(BwdParams p) {
         const bf16x8 bq = join8(ld_lds_tr4(dst_ + oD32[0]), ld_lds_tr4(dst_ + oD32[1]));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
       }
+      // hipcc has left only 11 of the 12 wait states a 32x32x16 result needs
+      // on the path that skips the odd step; a fixed pad covers every path
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 11" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
       acc += acc1;
       const int r = r0q + (lane & 31);
       if (r < p.rows) {
