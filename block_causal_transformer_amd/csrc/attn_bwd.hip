@@ -57,7 +57,6 @@
 // in both kernels) in exchange for no cross-workgroup sum of dQ.
 #include <algorithm>
 #include <mutex>
-#include <vector>
 
 #include "bca_device.h"
 #include "bca_kernels.h"
@@ -983,7 +982,7 @@ SplitPlan plan_split(const AttnDims& d) {
   SplitPlan sp;
   if (!bwd_uses_mfma(d) || uses_short(d) || attended_length(d) > kBwdKeyBlock) return sp;
   const int cus = device_cu_count();
-  const long problems = (long)(d.op == OP_SPACE ? d.B * d.T : d.B * d.N) * d.Hkv;
+  const long problems = (long)(d.op == OP_SPACE ? (long)d.B * d.T : (long)d.B * d.N) * d.Hkv;
   if (cus <= 0 || problems <= cus) return sp;
   const long tail = problems % cus;
   if (tail == 0 || tail > cus / 2) return sp;
@@ -992,26 +991,22 @@ SplitPlan plan_split(const AttnDims& d) {
   const int chunks = (int)((rows + KV_QC - 1) / KV_QC);
   const int nkt = (L + 15) / 16;
   if (chunks < 2) return sp;
-  std::vector<long> cost(chunks);
+  // key tiles a chunk sees: time attention, the tiles holding keys in
+  // [qlo - W + 1, qhi]; space attention, all of them
+  auto cost = [&](int c) -> long {
+    if (d.op != OP_TIME) return 28 + nkt;
+    const long qlo = (long)c * KV_QC / G;
+    const long qhi = (std::min<long>((long)c * KV_QC + KV_QC, rows) - 1) / G;
+    const long klo = d.window > 0 ? std::max<long>(0, qlo - d.window + 1) : 0;
+    const long t0 = klo / 16, t1 = std::min<long>(nkt - 1, qhi / 16);
+    return 28 + std::max<long>(0, t1 - t0 + 1);
+  };
   long total = 0;
-  for (int c = 0; c < chunks; ++c) {
-    const int qlo = (int)((long)c * KV_QC / G);
-    const int qhi = (int)((std::min<long>((long)c * KV_QC + KV_QC, rows) - 1) / G);
-    int seen = 0;
-    for (int t = 0; t < nkt; ++t) {
-      const int k0 = t * 16, k1 = std::min(k0 + 16, L);
-      bool none = false;
-      if (d.op == OP_TIME) none = k0 > qhi || (d.window > 0 && qlo - (k1 - 1) >= d.window);
-      seen += none ? 0 : 1;
-    }
-    cost[c] = 28 + seen;
-    total += cost[c];
-  }
-  long acc = 0;
+  for (int c = 0; c < chunks; ++c) total += cost(c);
+  long acc = 0, best_gap = -1;
   int best = 1;
-  long best_gap = -1;
   for (int c = 1; c < chunks; ++c) {
-    acc += cost[c - 1];
+    acc += cost(c - 1);
     const long gap = std::max(acc, total - acc);
     if (best_gap < 0 || gap < best_gap) {
       best_gap = gap;
