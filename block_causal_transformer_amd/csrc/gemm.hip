@@ -27,7 +27,10 @@
 //      1920-wide layers); it halves the LDS operand traffic per MFMA.
 //  Epilogues (both kernels): the QKV split (columns [0, nq) to Q, then K,
 //      then V, each row-major, which is the (B,T,N,H,D) layout of the
-//      attention inputs) and the residual add.
+//      attention inputs) and the residual add.  gemm256_kernel passes its
+//      results through LDS (16 rows per wave at a time) so that every lane
+//      stores 16 contiguous bytes and a wave's lanes run along its rows, and
+//      issues all of its residual loads before the first store.
 #include "bca_device.h"
 #include "bca_kernels.h"
 
@@ -81,6 +84,45 @@ __device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f3
     }
     *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(c));
   }
+}
+
+// Stores C[m][n .. n+7] (fp32 a, b) through epilogue EPI as one 16-byte
+// store; nothing past M or N (N and the QKV split points are multiples of 8).
+template <int EPI>
+__device__ __forceinline__ void store8(const GemmParams& p, int64_t m, int n, f32x4 a, f32x4 b) {
+  if (m >= p.M || n >= p.N) return;
+  bf16* dst;
+  if (EPI == 0) {
+    if (n < p.nq)
+      dst = p.out0 + m * p.nq + n;
+    else if (n < p.nq + p.nkv)
+      dst = p.out1 + m * p.nkv + (n - p.nq);
+    else
+      dst = p.out2 + m * p.nkv + (n - p.nq - p.nkv);
+  } else {
+    dst = p.out0 + m * p.N + n;
+    if (p.residual) {
+      const bf16x8 r = ld_global16(p.residual + m * p.N + n);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] += (float)r[e];
+        b[e] += (float)r[4 + e];
+      }
+    }
+  }
+  st_global16(dst, pack8(a, b));
+}
+
+// store8 for epilogue 1 with the residual piece already loaded (r)
+__device__ __forceinline__ void store8r(const GemmParams& p, int64_t m, int n, f32x4 a, f32x4 b,
+                                        const bf16x8& r) {
+  if (m >= p.M || n >= p.N) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] += (float)r[e];
+    b[e] += (float)r[4 + e];
+  }
+  st_global16(p.out0 + m * p.N + n, pack8(a, b));
 }
 
 template <int EPI>
@@ -326,14 +368,51 @@ void gemm256_kernel(GemmParams p) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the surplus reloads land before the workgroup ends
 
+  // The results leave through LDS, 16 rows at a time per wave, so that
+  // each lane stores (and, with a residual, loads) 16 contiguous bytes
+  // and consecutive lanes continue along a row: the accumulator layout
+  // would give 8-byte pieces 16 rows apart.  Every wave's direct-to-LDS
+  // loads have landed before the buffers are reused.
+  __syncthreads();
+  constexpr int CW = 16 * WTN;  // the wave's columns
+  constexpr int SP = CW + 4;    // padded row stride (floats): rows 4 banks apart
+  constexpr int PER = CW / 8;   // 8-column pieces per row
+  static_assert((16 * PER) % 64 == 0 && 4 * 16 * SP * 4 <= (int)sizeof(sA), "epilogue staging");
+  float* slab = reinterpret_cast<float*>(&sA[0][0]) + wave * 16 * SP;
+  const int64_t mw = m0 + wm * 128;
+  const int nw = n0 + wn * CW;
+  constexpr int IT = 16 * PER / 64;  // pieces per lane and 16-row round
+  // the residual pieces of every round, issued together (one latency)
+  constexpr bool PRE = EPI == 1;
+  bf16x8 res[PRE ? WT : 1][PRE ? IT : 1];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int j = 0; j < WT; ++j)
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int k = lane + 64 * it;
+        const int r = k / PER, c = (k - (k / PER) * PER) * 8;
+        const int64_t m = min(mw + j * 16 + r, p.M - 1);
+        res[j][it] = p.residual ? ld_global16(p.residual + m * p.N + min(nw + c, p.N - 8)) : zero8();
+      }
+  }
 #pragma unroll
   for (int j = 0; j < WT; ++j) {
-    // one m tile at a time: keeps the residual loads of later tiles from
-    // being hoisted into registers the accumulators still hold
     __builtin_amdgcn_sched_barrier(0);
-    const int64_t m = m0 + wm * 128 + j * 16 + li;
 #pragma unroll
-    for (int i = 0; i < WTN; ++i) store4<EPI>(p, m, n0 + wn * 16 * WTN + i * 16 + lg * 4, acc[i][j]);
+    for (int i = 0; i < WTN; ++i)
+      *reinterpret_cast<f32x4*>(slab + li * SP + i * 16 + lg * 4) = acc[i][j];
+#pragma unroll
+    for (int it = 0; it < 16 * PER / 64; ++it) {
+      const int k = lane + 64 * it;
+      const int r = k / PER, c = (k - (k / PER) * PER) * 8;
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(slab + r * SP + c);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(slab + r * SP + c + 4);
+      if constexpr (PRE)
+        store8r(p, mw + j * 16 + r, nw + c, v0, v1, res[j][it]);
+      else
+        store8<EPI>(p, mw + j * 16 + r, nw + c, v0, v1);
+    }
   }
 }
 
