@@ -21,12 +21,16 @@
 // statistics need only a 4-lane reduction; online softmax in the log2 domain
 // with a lazy rescale (a row's running reference max is moved only when one
 // of its new scores exceeds it by more than 2^8, which keeps exp2 arguments
-// <= 8; rows never rescale because of other rows' scores);
+// <= 8; rows never rescale because of other rows' scores; after a chunk's
+// first step the exps are formed first and that exact test runs only when
+// some lane's 8 exps of a row sum to more than 2^8);
 // O^T += V^T P^T on MFMA, V kept row-major in LDS (laid out as K, one 16-byte
 // write per piece when staged) and its V^T operand formed by transposing LDS
 // reads.  Fully masked key steps are never
 // visited (causal and window ranges), and per-element masks are applied only
 // on steps that straddle a mask edge.
+#include <type_traits>
+
 #include "bca_device.h"
 #include "bca_kernels.h"
 
@@ -166,6 +170,11 @@ void attn_fwd_kernel(FwdParams p) {
     // argument, and the raw-score threshold (m + 2^8 in log2 units, divided
     // by the scale) above which the row may need a new reference
     float negm[NQ], thr[NQ];
+    // and the bound on the sum of a lane's 8 exps of the row in one step
+    // above which the exact test runs: 2^8, or -1 (always) while the row
+    // has no reference yet
+    float lim[NQ];
+    bool fresh = true;  // no step of the chunk visited yet
     int qlo = 0, qhi = 0;
     if (active) {
 #pragma unroll
@@ -180,6 +189,7 @@ void attn_fwd_kernel(FwdParams p) {
         m[qt] = -INFINITY;
         negm[qt] = 0.f;
         thr[qt] = -INFINITY;
+        lim[qt] = -1.f;
         l[qt] = 0.f;
       }
       qlo = r0 / G + qsh;
@@ -236,98 +246,137 @@ void attn_fwd_kernel(FwdParams p) {
       khi = min(khi, key0 + kn);
       if (klo >= khi) continue;
       const int st0 = (klo - key0) >> 5, st1 = (khi - key0 + 31) >> 5;
-      for (int st = st0; st < st1; ++st) {
+      // one 32-key step; FIRST: the chunk's first visited step, which sets
+      // the rows' references before forming any exp
+      auto step = [&](int st, auto first_c) {
+        constexpr bool FIRST = decltype(first_c)::value;
         const int kabs = key0 + st * 32;
         // S^T tiles: rows = 16 keys (two halves of the step), columns = queries
         f32x4 sc[NQ][2];
+        auto scores = [&](int kst) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kr = st * 32 + h * 16 + li;
-          const bf16x8 k0 = ld_lds16(sK + k_off(kr, lg));
-          const bf16x8 k1 = ld_lds16(sK + k_off(kr, 4 + lg));
+          for (int h = 0; h < 2; ++h) {
+            const int kr = kst + h * 16 + li;
+            const bf16x8 k0 = ld_lds16(sK + k_off(kr, lg));
+            const bf16x8 k1 = ld_lds16(sK + k_off(kr, 4 + lg));
+#pragma unroll
+            for (int qt = 0; qt < NQ; ++qt) {
+              f32x4 z = {0.f, 0.f, 0.f, 0.f};
+              z = mfma16(k0, qreg[qt][0], z);
+              sc[qt][h] = mfma16(k1, qreg[qt][1], z);
+            }
+          }
+          // hipcc leaves as few as 7 wait states between these MFMAs and the
+          // first VALU read of sc along the branch paths below (8 are needed);
+          // a fixed pad covers every path
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("s_nop 7" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+          if (!tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
+            // a select, not a conditional store: hipcc dropped conditional
+            // element stores into this array of vectors
+#pragma unroll
+            for (int qt = 0; qt < NQ; ++qt) {
+              // time: the query sits at a real position (< L), so a key is
+              // visible iff 0 <= query - key < window (the whole sequence when
+              // there is none): one unsigned compare, and keys past the end
+              // fail it too
+              const int dq0 = qpos[qt] + qsh - kabs - lg * 4;
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  bool vis;
+                  if constexpr (MOP == OP_TIME)
+                    vis = (unsigned)(dq0 - h * 16 - j) < weff;
+                  else
+                    vis = visible_op<MOP>(md, qpos[qt] + qsh, kabs + h * 16 + lg * 4 + j);
+                  const float cur = sc[qt][h][j];
+                  sc[qt][h][j] = vis ? cur : -INFINITY;
+                }
+            }
+          }
+        };
+        scores(st * 32);
+        // The exps are formed against the current references first (except
+        // on the chunk's first step); a lane whose 8 exps of a row sum to at
+        // most 2^8 has none above 2^8, so none of its scores could move the
+        // reference, and only when some lane of the wave exceeds that bound
+        // does the wave form the scores again, run the exact test below and
+        // form the exps anew
+        f32x4 e0[NQ], e1[NQ];
+        float ls[NQ];  // sum of the lane's 8 exps of the row
+        auto form_exps = [&]() {
 #pragma unroll
           for (int qt = 0; qt < NQ; ++qt) {
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            z = mfma16(k0, qreg[qt][0], z);
-            sc[qt][h] = mfma16(k1, qreg[qt][1], z);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              e0[qt][j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, negm[qt]));
+              e1[qt][j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, negm[qt]));
+            }
+            ls[qt] = ((e0[qt][0] + e0[qt][1]) + (e0[qt][2] + e0[qt][3])) +
+                     ((e1[qt][0] + e1[qt][1]) + (e1[qt][2] + e1[qt][3]));
+          }
+        };
+        bool check = FIRST;
+        if constexpr (!FIRST) {
+          form_exps();
+          bool big = false;
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt) big |= ls[qt] > lim[qt];
+          check = __builtin_amdgcn_ballot_w64(big) != 0;
+          if (check) {
+            // the scores again rather than held through the exps (registers);
+            // the opaque offset keeps the compiler from reusing the first ones
+            int kst = st * 32;
+            asm volatile("" : "+s"(kst));
+            scores(kst);
           }
         }
-        // hipcc leaves as few as 7 wait states between these MFMAs and the
-        // first VALU read of sc along the branch paths below (8 are needed);
-        // a fixed pad covers every path
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_nop 7" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        if (!tile_all_visible(md, qlo, qhi, kabs, kabs + 32)) {
-          // a select, not a conditional store: hipcc dropped conditional
-          // element stores into this array of vectors
+        if (check) {
+          // online softmax with a lazy reference max (log2 domain): a row's
+          // reference moves only when one of its scores exceeds it by more
+          // than 2^8, and only that row is rescaled (the others multiply by
+          // exactly 1), so every row depends on its own scores alone
+          // each lane first tests its own 8 scores of the row; the 4-lane
+          // row maximum is formed only when some lane of the wave is over
+          float lmx[NQ];  // raw (unscaled) maximum of the lane's 8 scores of the row
+          bool over = false;
 #pragma unroll
           for (int qt = 0; qt < NQ; ++qt) {
-            // time: the query sits at a real position (< L), so a key is
-            // visible iff 0 <= query - key < window (the whole sequence when
-            // there is none): one unsigned compare, and keys past the end
-            // fail it too
-            const int dq0 = qpos[qt] + qsh - kabs - lg * 4;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                bool vis;
-                if constexpr (MOP == OP_TIME)
-                  vis = (unsigned)(dq0 - h * 16 - j) < weff;
-                else
-                  vis = visible_op<MOP>(md, qpos[qt] + qsh, kabs + h * 16 + lg * 4 + j);
-                const float cur = sc[qt][h][j];
-                sc[qt][h][j] = vis ? cur : -INFINITY;
-              }
+            const float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
+            const float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
+            lmx[qt] = fmaxf(a, b);
+            over |= lmx[qt] > thr[qt];
           }
-        }
-        // online softmax with a lazy reference max (log2 domain): a row's
-        // reference moves only when one of its scores exceeds it by more
-        // than 2^8, and only that row is rescaled (the others multiply by
-        // exactly 1), so every row depends on its own scores alone
-        // each lane first tests its own 8 scores of the row; the 4-lane
-        // row maximum is formed only when some lane of the wave is over
-        float lmx[NQ];  // raw (unscaled) maximum of the lane's 8 scores of the row
-        bool over = false;
+          if (__builtin_amdgcn_ballot_w64(over)) {
 #pragma unroll
-        for (int qt = 0; qt < NQ; ++qt) {
-          const float a = fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3]));
-          const float b = fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3]));
-          lmx[qt] = fmaxf(a, b);
-          over |= lmx[qt] > thr[qt];
-        }
-        if (__builtin_amdgcn_ballot_w64(over)) {
+            for (int qt = 0; qt < NQ; ++qt) {
+              // the scale is positive, so scaling commutes with the maximum
+              const float mx = group4_max(lmx[qt]) * p.scale_log2;
+              const bool grow = mx > m[qt] + kRescaleThreshold;
+              const float mn = grow ? mx : m[qt];
+              const float alpha = grow ? fast_exp2(m[qt] - mn) : 1.f;
+              l[qt] *= alpha;
 #pragma unroll
-          for (int qt = 0; qt < NQ; ++qt) {
-            // the scale is positive, so scaling commutes with the maximum
-            const float mx = group4_max(lmx[qt]) * p.scale_log2;
-            const bool grow = mx > m[qt] + kRescaleThreshold;
-            const float mn = grow ? mx : m[qt];
-            const float alpha = grow ? fast_exp2(m[qt] - mn) : 1.f;
-            l[qt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc[qt][dt] *= alpha;
-            m[qt] = mn;
-            negm[qt] = (mn == -INFINITY) ? 0.f : -mn;
-            // (the bound only decides when the test above runs; an ulp
-            // either way can change whether a score right at the threshold
-            // moves the reference, which the results do not depend on
-            // beyond rounding)
-            thr[qt] = (mn + kRescaleThreshold) * p.inv_scale_log2;
+              for (int dt = 0; dt < 4; ++dt) acc[qt][dt] *= alpha;
+              m[qt] = mn;
+              negm[qt] = (mn == -INFINITY) ? 0.f : -mn;
+              // (the bound only decides when the test above runs; an ulp
+              // either way can change whether a score right at the threshold
+              // moves the reference, which the results do not depend on
+              // beyond rounding)
+              thr[qt] = (mn + kRescaleThreshold) * p.inv_scale_log2;
+            lim[qt] = (mn == -INFINITY) ? -1.f : 256.f;
+            }
           }
+          form_exps();
         }
         bf16x8 pb[NQ];
 #pragma unroll
         for (int qt = 0; qt < NQ; ++qt) {
-          f32x4 e0, e1;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            e0[j] = fast_exp2(__builtin_fmaf(sc[qt][0][j], p.scale_log2, negm[qt]));
-            e1[j] = fast_exp2(__builtin_fmaf(sc[qt][1][j], p.scale_log2, negm[qt]));
-          }
-          l[qt] += ((e0[0] + e0[1]) + (e0[2] + e0[3])) + ((e1[0] + e1[1]) + (e1[2] + e1[3]));
-          pb[qt] = pack8(e0, e1);
+          l[qt] += ls[qt];
+          pb[qt] = pack8(e0[qt], e1[qt]);
         }
         // O^T += V^T P^T
 #pragma unroll
@@ -340,7 +389,13 @@ void attn_fwd_kernel(FwdParams p) {
 #pragma unroll
           for (int qt = 0; qt < NQ; ++qt) acc[qt][dt] = mfma16(vt, pb[qt], acc[qt][dt]);
         }
+      };
+      int st = st0;
+      if (fresh) {
+        fresh = false;
+        step(st++, std::true_type{});
       }
+      for (; st < st1; ++st) step(st, std::false_type{});
     }
 
     if (active) {
