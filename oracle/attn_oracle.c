@@ -339,22 +339,15 @@ int oracle_time_decode_fwd(int B, int Tq, int N, int Hq, int Hkv, int D, int win
  * are kept in fp32, bf16 covers most matmul activations and the attention
  * inputs, normalization layers stay in fp32.  Readings (the pages name no
  * norm and no layout): the norm before the QKV projection is an RMS norm with
- * a learned fp32 gain; its output is the bf16 matmul activation; weights are
- * bf16 copies stored (out_features, in_features); QKV output columns are the
- * Q heads, then the K heads, then the V heads; no biases.
- *
- * bf16(x): x rounded to the nearest value with 8 significant bits, ties to
- * even (finite, normal range). */
-static double round_bf16(double x) {
-  if (x == 0.0 || !isfinite(x)) return x;
-  int e;
-  const double m = frexp(x, &e);           /* x = m * 2^e, 0.5 <= |m| < 1 */
-  return ldexp(nearbyint(m * 256.0), e - 8); /* default rounding: to nearest even */
-}
+ * a learned fp32 gain, applied to the bf16 token rows; weights are bf16
+ * copies stored (out_features, in_features); QKV output columns are the Q
+ * heads, then the K heads, then the V heads; no biases.  The pages fix no
+ * rounding point inside norm-then-projection, so this is the exact product
+ * of the given bf16 and fp32 values. */
 
 /* RMS norm then the QKV projection.  x (M, dm); gamma (dm); w ((Hq+2Hkv)*D, dm);
  * q (M, Hq*D), k and v (M, Hkv*D); rstd (M) = 1/sqrt(mean(x^2) + eps).
- *   y = bf16(x * rstd * gamma),  [q | k | v] = y w^T. */
+ *   y = x * rstd * gamma,  [q | k | v] = y w^T. */
 int oracle_rmsnorm_qkv_fwd(long M, int dm, int Hq, int Hkv, int D, double eps,
                            const double* x, const double* gamma, const double* w,
                            double* q, double* k, double* v, double* rstd) {
@@ -368,7 +361,7 @@ int oracle_rmsnorm_qkv_fwd(long M, int dm, int Hq, int Hkv, int D, double eps,
     const double r = 1.0 / sqrt(ss / dm + eps);
     rstd[m] = r;
     double* y = (double*)malloc(sizeof(double) * dm);
-    for (int c = 0; c < dm; ++c) y[c] = round_bf16(xm[c] * r * gamma[c]);
+    for (int c = 0; c < dm; ++c) y[c] = xm[c] * r * gamma[c];
     for (int n = 0; n < nout; ++n) {
       const double acc = dot(y, w + (long)n * dm, dm);
       if (n < nq) q[m * nq + n] = acc;

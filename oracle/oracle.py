@@ -192,9 +192,9 @@ def bwd(w, q, k, v, dout, scale: float = 0.0, lib=None):
 
 def rmsnorm_qkv_fwd(x, gamma, w, Hq: int, Hkv: int, D: int, eps: float = 1e-6,
                     lib: Optional[ctypes.CDLL] = None):
-    """RMS norm (fp64, gain ``gamma``) rounded to bf16, then the QKV projection
-    with weight ``w`` ((Hq+2Hkv)*D, dm).  x is (M, dm).  Returns (q (M, Hq*D),
-    k (M, Hkv*D), v (M, Hkv*D), rstd (M,))."""
+    """RMS norm (fp64, gain ``gamma``), then the QKV projection with weight
+    ``w`` ((Hq+2Hkv)*D, dm), with no rounding in between.  x is (M, dm).
+    Returns (q (M, Hq*D), k (M, Hkv*D), v (M, Hkv*D), rstd (M,))."""
     h = lib or load()
     x, gamma, w = _f64(x), _f64(gamma), _f64(w)
     M, dm = x.shape

@@ -18,7 +18,7 @@ disagrees with what the mathematics or the pages fix:
 * rollout decode: torch SDPA over the ring positions with a mask built from
   the frame each position holds, and row t of time attention over the whole
   sequence;
-* projections: torch fp64 ``F.rms_norm``, the bf16 cast and a matmul; the
+* projections: torch fp64 ``F.rms_norm`` and a matmul; the
   RMS norm's exact invariance to a power-of-two input scale; identity
   weights.
 """
@@ -496,8 +496,7 @@ def pin_decode_matches_full_sequence(lib):
 # ---------------------------------------------------------- projections
 
 def pin_rmsnorm_qkv_torch(lib):
-    """RMS norm + bf16 rounding + QKV projection against torch fp64
-    (F.rms_norm, the bf16 cast, a matmul)."""
+    """RMS norm + QKV projection against torch fp64 (F.rms_norm, a matmul)."""
     for i, (M, dm, Hq, Hkv, D, eps) in enumerate(((7, 48, 4, 2, 8, 1e-6), (5, 40, 3, 1, 8, 1e-3),
                                                   (3, 64, 2, 2, 16, 0.0))):
         x = rnd((M, dm), 610 + i, 3.0)
@@ -506,8 +505,7 @@ def pin_rmsnorm_qkv_torch(lib):
         q, k, v, rstd = O.rmsnorm_qkv_fwd(x, g, w, Hq, Hkv, D, eps, lib=lib)
         xt = torch.tensor(x)
         y = F.rms_norm(xt, (dm,), torch.tensor(g), eps=eps)
-        yb = y.to(torch.bfloat16).to(torch.float64)
-        out = (yb @ torch.tensor(w).T).numpy()
+        out = (y @ torch.tensor(w).T).numpy()
         close(q, out[:, :Hq * D], 1e-12, "qkv case %d q" % i)
         close(k, out[:, Hq * D:(Hq + Hkv) * D], 1e-12, "qkv case %d k" % i)
         close(v, out[:, (Hq + Hkv) * D:], 1e-12, "qkv case %d v" % i)
