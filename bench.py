@@ -71,7 +71,7 @@ KERNELS = {
                  "+ attn_bwd_split_reduce_kernel<0> when the last round is split]",
     "time_bwd": "attn_bwd_dkv_kernel<1, TPW, FQ> [+ attn_bwd_dq_kernel<1> past 320 keys, "
                 "+ attn_bwd_split_reduce_kernel<1> when the last round is split]",
-    "qkv_proj": "rmsnorm_rows_kernel + gemm256_kernel<0, 8>",
+    "qkv_proj": "rstd_rows_kernel + fold_gain_kernel + gemm256_kernel<0, 8>",
     "out_proj": "gemm256_kernel<1, 6>",
 }
 

@@ -277,7 +277,7 @@ size_t bca_qkv_workspace_bytes(const bca_proj_shape* shape) {
     g_last_error = saved;
     return 0;
   }
-  return (size_t)d.M * d.d_model * 2;
+  return bca::qkv_workspace_bytes(d);
 }
 
 int rmsnorm_qkv_fwd(const bca_proj_shape* shape, const void* x, const float* gain, float eps,
@@ -292,7 +292,7 @@ int rmsnorm_qkv_fwd(const bca_proj_shape* shape, const void* x, const float* gai
   st = check_ptrs(names, ptrs, 7);
   if (st) return st;
   if (rstd && !aligned16(rstd)) return fail(BCA_ERR_INVALID_ARG, "pointer 'rstd' is not 16-byte aligned");
-  const size_t need = (size_t)d.M * d.d_model * 2;
+  const size_t need = bca::qkv_workspace_bytes(d);
   if (workspace_bytes < need)
     return fail(BCA_ERR_INVALID_ARG, "workspace of %zu bytes is smaller than the %zu required",
                 workspace_bytes, need);

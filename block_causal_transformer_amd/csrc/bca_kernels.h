@@ -95,7 +95,14 @@ struct ProjDims {
   int d_model, Hq, Hkv, D;
 };
 
-// RMS norm (into `workspace`, M * d_model bf16) then the QKV projection.
+// RMS norm then the QKV projection: the gain is folded into a bf16 copy of
+// the weights in `workspace` (qkv_workspace_bytes: that copy, then M fp32
+// rstd values used when `rstd` is NULL), the rows' rstd scales the fp32 sums.
+inline size_t qkv_weight_bytes(const ProjDims& d) {
+  const size_t b = (size_t)(d.Hq + 2 * d.Hkv) * d.D * d.d_model * 2;
+  return (b + 255) & ~(size_t)255;  // rstd starts 256-byte aligned
+}
+inline size_t qkv_workspace_bytes(const ProjDims& d) { return qkv_weight_bytes(d) + (size_t)d.M * 4; }
 hipError_t launch_rmsnorm_qkv(const ProjDims& d, const void* x, const float* gain, float eps,
                               const void* w, void* q, void* k, void* v, float* rstd,
                               void* workspace, hipStream_t stream);

@@ -5,12 +5,13 @@
 // heads of width 64) and section "Ingénierie de la stabilité", item 3
 // (parameters in fp32, bf16 for most matmul activations and the attention
 // inputs, fp32 for normalization layers).  The norm before the QKV projection
-// is an RMS norm with an fp32 gain whose output, rounded to bf16, is the
-// matmul activation; weights are bf16, stored (out_features, in_features).
+// is an RMS norm with an fp32 gain; weights are bf16, stored (out_features,
+// in_features).  The normalized rows are never stored: the gain goes into a
+// bf16 copy of the weights and each row's fp32 rstd scales its fp32 sums.
 //
-//  rmsnorm_rows_kernel: one wave per token row (held in registers up to
-//      2048 features): fp32 sum of squares, rstd = 1/sqrt(mean + eps),
-//      y = bf16(x * rstd * gain) into a workspace.
+//  rstd_rows_kernel: one wave per token row: fp32 sum of squares,
+//      rstd = 1/sqrt(mean + eps).
+//  fold_gain_kernel: wg = bf16(w * gain) (the gain along the K dimension).
 //  gemm_nt_kernel: C = A B^T for A (M, K) and B (N, K), both K-contiguous,
 //      fp32 accumulation, bf16 results.  A 128 x 128 output tile per
 //      workgroup of 4 waves (64 x 64 each), K in steps of 64 through
@@ -27,7 +28,8 @@
 //      1920-wide layers); it halves the LDS operand traffic per MFMA.
 //  Epilogues (both kernels): the QKV split (columns [0, nq) to Q, then K,
 //      then V, each row-major, which is the (B,T,N,H,D) layout of the
-//      attention inputs) and the residual add.  gemm256_kernel passes its
+//      attention inputs) with each row scaled by its rstd, and the residual
+//      add.  gemm256_kernel passes its
 //      results through LDS (16 rows per wave at a time) so that every lane
 //      stores 16 contiguous bytes and a wave's lanes run along its rows, and
 //      issues all of its residual loads before the first store.
@@ -56,10 +58,22 @@ struct GemmParams {
   const bf16* residual;
   int nq, nkv;
   int mtiles, ntiles;
+  // epilogue 0 (QKV after the RMS norm): each row of C is scaled by its rstd
+  const float* rstd_in;
 };
 
 __device__ __forceinline__ int tile_off(int row, int chunk) {  // [rows][64] bf16, 16B chunks xor-swizzled
   return row * GBK + ((chunk ^ (row & 7)) << 3);
+}
+
+// s plus the sum of squares of v's 8 values (fp32, by bf16 pairs: each
+// square is exact in fp32)
+__device__ __forceinline__ float sumsq8(const bf16x8& v, float s) {
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), __builtin_shufflevector(v, v, 0, 1), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), __builtin_shufflevector(v, v, 2, 3), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), __builtin_shufflevector(v, v, 4, 5), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), __builtin_shufflevector(v, v, 6, 7), s, false);
+  return s;
 }
 
 // Stores C[m][n .. n+3] (fp32 c) through epilogue EPI; nothing past M or N.
@@ -67,6 +81,7 @@ template <int EPI>
 __device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f32x4 c) {
   if (m >= p.M || n >= p.N) return;
   if (EPI == 0) {
+    c *= p.rstd_in[m];
     bf16* dst;
     if (n < p.nq)
       dst = p.out0 + m * p.nq + n;
@@ -88,11 +103,15 @@ __device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f3
 
 // Stores C[m][n .. n+7] (fp32 a, b) through epilogue EPI as one 16-byte
 // store; nothing past M or N (N and the QKV split points are multiples of 8).
+// Epilogue 0 scales the row by its rstd.
 template <int EPI>
 __device__ __forceinline__ void store8(const GemmParams& p, int64_t m, int n, f32x4 a, f32x4 b) {
   if (m >= p.M || n >= p.N) return;
   bf16* dst;
   if (EPI == 0) {
+    const float rs = p.rstd_in[m];
+    a *= rs;
+    b *= rs;
     if (n < p.nq)
       dst = p.out0 + m * p.nq + n;
     else if (n < p.nq + p.nkv)
@@ -416,66 +435,52 @@ void gemm256_kernel(GemmParams p) {
   }
 }
 
-// One wave per row: fp32 sum of squares over the row, then the scaled,
-// gained values rounded to bf16.  Rows are d_model elements, d_model % 8 ==
-// 0.  Rows of up to 64 * 8 * RC elements stay in registers between the two
-// passes (one read of x); longer rows are read twice.
-template <int RC>
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const bf16* x, const float* gain, float eps,
-                                                           int64_t M, int dm, bf16* y, float* rstd_out) {
+// One wave per row: rstd = 1/sqrt(mean(x^2) + eps) in fp32.  Rows are
+// d_model elements, d_model % 8 == 0.
+__global__ __launch_bounds__(256) void rstd_rows_kernel(const bf16* x, float eps, int64_t M, int dm,
+                                                        float* rstd_out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   const bf16* xr = x + row * dm;
-  bf16* yr = y + row * dm;
   const int nch = dm >> 3;
-  bf16x8 held[RC];
   float ss = 0.f;
-  if (nch <= 64 * RC) {
+  // four 16-byte pieces per lane in flight at once (rows of up to 2048)
+  int c = lane;
+  for (; c + 192 < nch; c += 256) {
+    bf16x8 v[4];
 #pragma unroll
-    for (int i = 0; i < RC; ++i) {
-      const int c = lane + 64 * i;
-      held[i] = c < nch ? ld_global16(xr + c * 8) : zero8();
+    for (int i = 0; i < 4; ++i) v[i] = ld_global16(xr + (c + 64 * i) * 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = (float)held[i][e];
-        ss = __builtin_fmaf(f, f, ss);
-      }
-    }
-  } else {
-    for (int c = lane; c < nch; c += 64) {
-      const bf16x8 v = ld_global16(xr + c * 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float f = (float)v[e];
-        ss = __builtin_fmaf(f, f, ss);
-      }
-    }
+    for (int i = 0; i < 4; ++i) ss = sumsq8(v[i], ss);
   }
+  bf16x8 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = c + 64 * i < nch ? ld_global16(xr + (c + 64 * i) * 8) : zero8();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ss = sumsq8(v[i], ss);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-  const float r = 1.0f / sqrtf(ss / (float)dm + eps);
-  if (lane == 0 && rstd_out) rstd_out[row] = r;
-  auto put = [&](int c, const bf16x8& v) {
-    const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + c * 8);
-    const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + c * 8 + 4);
-    f32x4 a, b;
+  if (lane == 0) rstd_out[row] = 1.0f / sqrtf(ss / (float)dm + eps);
+}
+
+// The RMS norm's gain folded into the QKV weights: wf[n][c] = bf16(w[n][c] *
+// gain[c]), one thread per 8 elements (K % 8 == 0).
+__global__ __launch_bounds__(256) void fold_gain_kernel(const bf16* w, const float* gain, int64_t count,
+                                                        int K, bf16* wf) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  const int c = (int)((i * 8) % K);
+  const bf16x8 v = ld_global16(w + i * 8);
+  const f32x4 g0 = *reinterpret_cast<const f32x4*>(gain + c);
+  const f32x4 g1 = *reinterpret_cast<const f32x4*>(gain + c + 4);
+  f32x4 a, b;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = (float)v[e] * r * g0[e];
-      b[e] = (float)v[4 + e] * r * g1[e];
-    }
-    st_global16(yr + c * 8, pack8(a, b));
-  };
-  if (nch <= 64 * RC) {
-#pragma unroll
-    for (int i = 0; i < RC; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nch) put(c, held[i]);
-    }
-  } else {
-    for (int c = lane; c < nch; c += 64) put(c, ld_global16(xr + c * 8));
+  for (int e = 0; e < 4; ++e) {
+    a[e] = (float)v[e] * g0[e];
+    b[e] = (float)v[4 + e] * g1[e];
   }
+  st_global16(wf + i * 8, pack8(a, b));
 }
 
 hipError_t launch_gemm(GemmParams& p, int epi, hipStream_t stream) {
@@ -500,16 +505,8 @@ hipError_t launch_gemm(GemmParams& p, int epi, hipStream_t stream) {
 hipError_t launch_rmsnorm_qkv(const ProjDims& d, const void* x, const float* gain, float eps,
                               const void* w, void* q, void* k, void* v, float* rstd,
                               void* workspace, hipStream_t stream) {
-  bf16* y = static_cast<bf16*>(workspace);
-  const int64_t blocks = (d.M + 3) / 4;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_rows_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     static_cast<const bf16*>(x), gain, eps, d.M, d.d_model, y, rstd);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   GemmParams p{};
-  p.a = y;
-  p.b = static_cast<const bf16*>(w);
+  p.a = static_cast<const bf16*>(x);
   p.M = d.M;
   p.N = (d.Hq + 2 * d.Hkv) * d.D;
   p.K = d.d_model;
@@ -518,6 +515,22 @@ hipError_t launch_rmsnorm_qkv(const ProjDims& d, const void* x, const float* gai
   p.out2 = static_cast<bf16*>(v);
   p.nq = d.Hq * d.D;
   p.nkv = d.Hkv * d.D;
+  // workspace: the gain-folded weights, then room for rstd
+  bf16* wf = static_cast<bf16*>(workspace);
+  float* rs = rstd ? rstd : reinterpret_cast<float*>(static_cast<char*>(workspace) + qkv_weight_bytes(d));
+  const int64_t n8 = (int64_t)p.N * p.K / 8;
+  hipLaunchKernelGGL(fold_gain_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const bf16*>(w), gain, n8, p.K, wf);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  p.b = wf;
+  const int64_t blocks = (d.M + 3) / 4;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rstd_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p.a, eps, d.M,
+                     d.d_model, rs);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  p.rstd_in = rs;
   return launch_gemm(p, 0, stream);
 }
 

@@ -40,7 +40,8 @@ OPS = [
     (r"attn_bwd_dkv_kernel<1[,>]", "time_bwd"),
     (r"attn_bwd_split_reduce_kernel<0>", "space_bwd"),
     (r"attn_bwd_split_reduce_kernel<1>", "time_bwd"),
-    (r"rmsnorm_rows_kernel", "qkv_proj"),
+    (r"rstd_rows_kernel", "qkv_proj"),
+    (r"fold_gain_kernel", "qkv_proj"),
     (r"gemm256_kernel<0[,>]", "qkv_proj"),
     (r"gemm_nt_kernel<0>", "qkv_proj"),
     (r"gemm256_kernel<1[,>]", "out_proj"),

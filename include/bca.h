@@ -222,13 +222,17 @@ typedef struct {
   int32_t D;        /* head width; multiple of 8 */
 } bca_proj_shape;
 
-/* Device workspace rmsnorm_qkv_fwd needs: the bf16 normalized activation,
- * M * d_model * 2 bytes (0 for an invalid shape). */
+/* Device workspace rmsnorm_qkv_fwd needs (0 for an invalid shape): a bf16
+ * copy of w_qkv with the gain folded in, (Hq + 2 Hkv) * D * d_model * 2 bytes
+ * rounded up to a multiple of 256, then M fp32 rstd values (used when the
+ * caller passes no rstd). */
 size_t bca_qkv_workspace_bytes(const bca_proj_shape* shape);
 
 /* RMS norm then the QKV projection (no biases):
- *   rstd = 1/sqrt(mean_c x[m][c]^2 + eps),  y = bf16(x * rstd * gain)   (fp32)
- *   [q | k | v][m] = y[m] w_qkv^T            (bf16 operands, fp32 sums)
+ *   rstd = 1/sqrt(mean_c x[m][c]^2 + eps)                              (fp32)
+ *   [q | k | v][m] = (x[m] * rstd[m] * gain) w_qkv^T
+ * computed as rstd[m] * (x[m] wg^T) with wg = bf16(w_qkv * gain) formed in
+ * the workspace (bf16 operands, fp32 sums, bf16 results).
  *   x      (M, d_model) bf16            gain  (d_model) fp32
  *   w_qkv  ((Hq + 2 Hkv) * D, d_model)  rows: the Q heads, the K heads, the V heads
  *   q      (M, Hq * D), k, v (M, Hkv * D) bf16: with M = B*T*N these are the

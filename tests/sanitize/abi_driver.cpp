@@ -175,7 +175,7 @@ int main() {
   {
     bca_proj_shape ps = {74240, 1920, 30, 3, 64};
     const size_t w = bca_qkv_workspace_bytes(&ps);
-    EXPECT(w == (size_t)74240 * 1920 * 2);
+    EXPECT(w == ((size_t)2304 * 1920 * 2 + 255) / 256 * 256 + (size_t)74240 * 4);  // folded weights, rstd
     EXPECT(rmsnorm_qkv_fwd(&ps, P, static_cast<float*>(P), 1e-6f, P, P, P, P, nullptr, P, w, nullptr) == BCA_OK);
     EXPECT(rmsnorm_qkv_fwd(&ps, P, static_cast<float*>(P), -1.f, P, P, P, P, nullptr, P, w, nullptr) ==
            BCA_ERR_INVALID_ARG);

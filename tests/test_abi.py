@@ -207,7 +207,12 @@ def qkv_call(shape, eps=1e-6, ptrs=None, rstd=None, ws_bytes=None):
 
 
 def test_projection_workspace_query(lib):
-    assert ops.bca_qkv_workspace_bytes(proj_shape()) == 300 * 1920 * 2
+    # the gain-folded weights ((30 + 2 * 3) * 64 rows of 1920, 256-byte aligned),
+    # then an fp32 rstd per row
+    wbytes = (30 + 2 * 3) * 64 * 1920 * 2
+    assert ops.bca_qkv_workspace_bytes(proj_shape()) == (wbytes + 255) // 256 * 256 + 300 * 4
+    assert ops.bca_qkv_workspace_bytes(proj_shape(M=7, d_model=72, Hq=2, Hkv=1, D=8)) == \
+        ((2 + 2) * 8 * 72 * 2 + 255) // 256 * 256 + 7 * 4
     assert ops.bca_qkv_workspace_bytes(proj_shape(M=0)) == 0
     assert ops.bca_qkv_workspace_bytes(proj_shape(d_model=100)) == 0
     assert ops.bca_qkv_workspace_bytes(None) == 0
