@@ -416,7 +416,9 @@ __device__ __forceinline__ int ds_off(int key, int row) {  // [KMAX][32]
 // holding agent keys use, so P of a hidden pair is exp2(-inf) = 0 exactly.
 // Keys past the end need no mask: they only feed their own (discarded) dK, dV
 // columns and, with FQ, dQ through K rows that are zero in LDS.
-template <int OP, int TPW, bool FQ>
+// GC > 0: an instance for G = GC query heads per KV head (the chunk
+// positions then divide by a constant instead of a runtime G).
+template <int OP, int TPW, bool FQ, int GC = 0>
 __global__ __attribute__((amdgpu_flat_work_group_size(kv_waves<TPW>() * 64, kv_waves<TPW>() * 64),
                           amdgpu_waves_per_eu(kv_waves<TPW>() / 4, kv_waves<TPW>() / 4)))
 void attn_bwd_dkv_kernel(BwdParams p) {
@@ -444,8 +446,10 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, 64);
   const UnitGeom gl = unit_geom(OP, u, p.T, p.N, p.Hq, 1);
   const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
-  const int G = p.G;
+  const int G = GC > 0 ? GC : p.G;
   const int64_t qhead = (int64_t)g * G * 64;
+  // position of folded row r >= 0
+  auto pos_of = [&](int r) { return GC > 0 ? (int)((unsigned)r / (unsigned)GC) : row_pos(r, p.inv_g); };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -523,7 +527,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     pre_valid = r < p.rows;
     if constexpr (OP == OP_SPACE) pre_agent = (unsigned)(r - agentG0) < agentGn;
     const int rr = min(r, p.rows - 1);
-    const int pos = row_pos(rr, p.inv_g);
+    const int pos = pos_of(rr);
     const int hh = rr - pos * G;
     const int64_t off = gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + sch * 8;
     const int64_t lo = gl.base + (int64_t)pos * gl.pos_stride + g * G + hh;
@@ -659,7 +663,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       // lane (li, lg): row hq*16 + li of the chunk, head dims dsl*16 + 4 lg ..
       const int r = r0q + hq * 16 + li;
       if (r < p.rows) {
-        const int pos = row_pos(r, p.inv_g);
+        const int pos = pos_of(r);
         const int hh = r - pos * G;
         bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + dsl * 16 + lg * 4;
         *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(acc * p.scale));
@@ -723,7 +727,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       acc += acc1;
       const int r = r0q + (lane & 31);
       if (r < p.rows) {
-        const int pos = row_pos(r, p.inv_g);
+        const int pos = pos_of(r);
         const int hh = r - pos * G;
         bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + 32 * (wave & 1) + 4 * (lane >> 5);
 #pragma unroll
@@ -1149,7 +1153,9 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
       hipLaunchKernelGGL(attn_bwd_split_reduce_kernel<OP_SPACE>, dim3((unsigned)((sp.count * (long)p.L * 16 + 255) / 256)),
                          dim3(256), 0, stream, p, sp.count);
   } else {
-    if (tpw == 1)
+    if (tpw == 1 && p.G == 10)  // the dynamics model's 30 query heads over 3
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true, 10>), g2d, bw, 0, stream, p);
+    else if (tpw == 1)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true>), g2d, bw, 0, stream, p);
     else if (fq)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), g2d, b8, 0, stream, p);
