@@ -448,8 +448,9 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
   const int G = GC > 0 ? GC : p.G;
   const int64_t qhead = (int64_t)g * G * 64;
-  // position of folded row r >= 0
+  // position of folded row r >= 0, and r / G on the scalar unit
   auto pos_of = [&](int r) { return GC > 0 ? (int)((unsigned)r / (unsigned)GC) : row_pos(r, p.inv_g); };
+  auto div_g = [&](int r) { return GC > 0 ? (int)((unsigned)r / (unsigned)GC) : r / G; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -645,7 +646,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     if constexpr (FQ) {
       if (KV_W > 8 && wave >= 8) return;
       const int r0q = cq * KV_QC;
-      const int qlo = r0q / G, qhi = (min(r0q + KV_QC, p.rows) - 1) / G;
+      const int qlo = div_g(r0q), qhi = div_g(min(r0q + KV_QC, p.rows) - 1);
       int klo, khi;
       key_range(md, qlo, qhi, klo, khi);
       const int st0 = max(klo - kb0, 0) >> 5, st1 = (min(khi, kend) - kb0 + 31) >> 5;
@@ -693,7 +694,7 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     if constexpr (DQ32) {
       if (wave < 6) return;
       const int r0q = cq * KV_QC;
-      const int qlo = r0q / G, qhi = (min(r0q + KV_QC, p.rows) - 1) / G;
+      const int qlo = div_g(r0q), qhi = div_g(min(r0q + KV_QC, p.rows) - 1);
       int klo, khi;
       key_range(md, qlo, qhi, klo, khi);
       const int s0 = max(klo - kb0, 0) >> 4, s1 = (min(khi, kend) - kb0 + 15) >> 4;
@@ -755,8 +756,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     KvBuf& b = sbuf[c & 1];
     const char* bb = reinterpret_cast<const char*>(&b);
     const int r0 = c * KV_QC;
-    const int qlo = r0 / G;
-    const int qhi = (min(r0 + KV_QC, p.rows) - 1) / G;
+    const int qlo = div_g(r0);
+    const int qhi = div_g(min(r0 + KV_QC, p.rows) - 1);
     bool work[TPW], edge[TPW];
     bool anyw = false;
 #pragma unroll
@@ -1142,6 +1143,8 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   if (d.op == OP_SPACE) {
     if (fq && tpw == 2)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 2, true>), g2d, b8, 0, stream, p);
+    else if (fq && p.G == 10)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, true, 10>), g2d, b8, 0, stream, p);
     else if (fq)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_SPACE, 3, true>), g2d, b8, 0, stream, p);
     else if (tpw == 2)
