@@ -673,18 +673,22 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   };
   // DQ32: wave 6 + a forms the 32 x 32 block of the chunk's dQ^T for head
   // dims 32a .. 32a + 31 (all 32 rows) on v_mfma_f32_32x32x16_bf16, over
-  // 16-key steps.  Operand layout: lane l holds row l % 32 of A (head dim)
-  // and column l % 32 of B (query row) for contraction indices (keys)
-  // 8 (l / 32) .. +7, each as two transposing reads of 4 keys; the output
-  // lane l holds query row l % 32, head dims 8 q + 4 (l / 32) + j (q, j <
-  // 4) of the block.
+  // 16-key steps.  Operand layout: lane l holds row l % 32 of A and column
+  // l % 32 of B (query row) for contraction indices (keys) 8 (l / 32) ..
+  // +7, each as two transposing reads of 4 keys.  A's row rho is head dim
+  // 32a + 16 ((rho >> 2) & 1) + 4 (rho >> 3) + (rho & 3), so that the output
+  // lane l, which holds rows 8 q + 4 (l / 32) + j (q, j < 4), ends with the
+  // 16 consecutive dims 32a + 16 (l / 32) .. +15 of query row l % 32 (two
+  // 16-byte stores).  In the transposing reads, lane i of a 16-lane group
+  // receives the dim that the lanes with i' & 3 == i >> 2 address, plus
+  // i & 3.
   int oK32[2] = {0, 0}, oD32[2] = {0, 0};
   if constexpr (DQ32) {
     const int g16 = lane >> 4, i16 = lane & 15;
     const int kq = 8 * (g16 >> 1) + (i16 >> 2);  // key of this lane's piece (+4 for the second)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      oK32[e] = kq_off(kq + 4 * e, 32 * (wave & 1) + 16 * (g16 & 1) + 4 * (i16 & 3));
+      oK32[e] = kq_off(kq + 4 * e, 32 * (wave & 1) + 8 * (g16 & 1) + 16 * (i16 & 1) + 4 * ((i16 >> 1) & 1));
       oD32[e] = ds_off(kq + 4 * e, 16 * (g16 & 1) + 4 * (i16 & 3));
     }
 #pragma unroll
@@ -730,13 +734,14 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       if (r < p.rows) {
         const int pos = pos_of(r);
         const int hh = r - pos * G;
-        bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + 32 * (wave & 1) + 4 * (lane >> 5);
+        bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + 32 * (wave & 1) + 16 * (lane >> 5);
+        f32x4 v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {acc[4 * q] * p.scale, acc[4 * q + 1] * p.scale, acc[4 * q + 2] * p.scale,
-                           acc[4 * q + 3] * p.scale};
-          *reinterpret_cast<u32x2*>(dst + 8 * q) = __builtin_bit_cast(u32x2, pack4(v));
-        }
+        for (int q = 0; q < 4; ++q)
+          v[q] = f32x4{acc[4 * q] * p.scale, acc[4 * q + 1] * p.scale, acc[4 * q + 2] * p.scale,
+                       acc[4 * q + 3] * p.scale};
+        st_global16(dst, pack8(v[0], v[1]));
+        st_global16(dst + 8, pack8(v[2], v[3]));
       }
     }
   };
