@@ -301,9 +301,11 @@ void attn_bwd_dq_kernel(BwdParams p) {
             dsb[qt] = pack8(d0, d1);
           }
         }
+        // tile dt's operand row r is head dim 16 (r >> 2) + 4 dt + (r & 3),
+        // so that each lane ends with dims 16 lg .. 16 lg + 15 of its row
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 kt = ld_lds16(sm.KT + kt_off(dt * 16 + li, st * 32 + lg * 8));
+          const bf16x8 kt = ld_lds16(sm.KT + kt_off(16 * (li >> 2) + 4 * dt + (li & 3), st * 32 + lg * 8));
           acc[dt][0] = mfma16(kt, dsb[0], acc[dt][0]);
           acc[dt][1] = mfma16(kt, dsb[1], acc[dt][1]);
         }
@@ -313,10 +315,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       if (!qv[qt]) continue;
-      bf16* dst = p.dq + gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 4;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        *reinterpret_cast<u32x2*>(dst + dt * 16) = __builtin_bit_cast(u32x2, pack4(acc[dt][qt] * p.scale));
+      bf16* dst = p.dq + gq.base + (int64_t)qpos[qt] * gq.pos_stride + qhead + hh[qt] * 64 + lg * 16;
+      st_global16(dst, pack8(acc[0][qt] * p.scale, acc[1][qt] * p.scale));
+      st_global16(dst + 8, pack8(acc[2][qt] * p.scale, acc[3][qt] * p.scale));
     }
   }
 }
