@@ -539,7 +539,8 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       pre = ld_global16(p.dout + off);
       pre_o = ld_global16(p.o + off);
     } else {
-      pre = ld_global16((carries_q ? p.q : p.dout) + off);
+      // (the base chosen per wave, a scalar select: the same as carries_q)
+      pre = ld_global16((((wave & 7) < 4) ? p.q : p.dout) + off);
       if (carries_q)
         pre_s = p.lse[lo];
       else
@@ -621,9 +622,13 @@ void attn_bwd_dkv_kernel(BwdParams p) {
       st_lds16(sm.K + kq_off(r, ch * 8), kv);
     }
   }
-  // FQ, dQ of chunk cq from its dS buffer: wave w forms the 16 x 16 block of
-  // dQ^T for head-dim slice w & 3 and row half w >> 2, over the 32-key steps
-  // that hold the chunk's visible keys
+  // FQ, dQ of chunk cq from its dS buffer, over the 32-key steps that hold
+  // the chunk's visible keys: with 8 waves, wave w forms the 16 x 16 block
+  // of dQ^T for head-dim slice w & 3 and row half w >> 2; with 16, waves 0..3
+  // form two such blocks each, for row half w >> 1 and the 32 dims from 32 (w
+  // & 1), whose operand rows are permuted (block t, row r: dim 32 (w & 1) + 8
+  // (r >> 2) + 4 t + (r & 3)) so that each lane ends with 8 consecutive dims
+  // of its row and stores them as one 16-byte piece
   // Lane offsets (elements) into the swizzled K and dS buffers, formed once:
   // the swizzles depend only on key bits 1..3, so moving by 16 keys (a tile)
   // or 32 (a dQ step) adds a constant.  dQ reads: key 8 lg + (li >> 2) (+4)
@@ -635,8 +640,15 @@ void attn_bwd_dkv_kernel(BwdParams p) {
     const int kq = 8 * lg + (li >> 2);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      oK[e] = kq_off(kq + 4 * e, (wave & 3) * 16 + 4 * (li & 3));
-      oD[e] = ds_off(kq + 4 * e, (wave >> 2) * 16 + 4 * (li & 3));
+      if constexpr (KV_W > 8) {
+        // block 1's dims are block 0's + 4, which in kq_off's swizzle (even
+        // 4-dim piece index, xor on bits 2..3 of it) is 4 elements further
+        oK[e] = kq_off(kq + 4 * e, 32 * (wave & 1) + 8 * (li & 3));
+        oD[e] = ds_off(kq + 4 * e, ((wave >> 1) & 1) * 16 + 4 * (li & 3));
+      } else {
+        oK[e] = kq_off(kq + 4 * e, (wave & 3) * 16 + 4 * (li & 3));
+        oD[e] = ds_off(kq + 4 * e, (wave >> 2) * 16 + 4 * (li & 3));
+      }
       oW[e] = ds_off(li, e * 16 + 4 * lg);
       oB[e] = kq_off(li, (4 * e + lg) * 8);
     }
@@ -645,15 +657,14 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   }
   auto dq_phase = [&](int cq) {
     if constexpr (FQ) {
-      if (KV_W > 8 && wave >= 8) return;
+      if (wave >= (KV_W > 8 ? 4 : 8)) return;
       const int r0q = cq * KV_QC;
       const int qlo = div_g(r0q), qhi = div_g(min(r0q + KV_QC, p.rows) - 1);
       int klo, khi;
       key_range(md, qlo, qhi, klo, khi);
       const int st0 = max(klo - kb0, 0) >> 5, st1 = (min(khi, kend) - kb0 + 31) >> 5;
-      const int dsl = wave & 3, hq = wave >> 2;
       const bf16* dsb = sm.dS[cq & 1];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       for (int st = st0; st < st1; ++st) {
         // four head-dim columns of K and four rows of dS per lane and read
         const bf16* kst = sm.K + st * 32 * 64;
@@ -661,14 +672,29 @@ void attn_bwd_dkv_kernel(BwdParams p) {
         const bf16x8 a = join8(ld_lds_tr4(kst + oK[0]), ld_lds_tr4(kst + oK[1]));
         const bf16x8 bq = join8(ld_lds_tr4(dst_ + oD[0]), ld_lds_tr4(dst_ + oD[1]));
         acc = mfma16(a, bq, acc);
+        if constexpr (KV_W > 8) {
+          const bf16x8 a1 = join8(ld_lds_tr4(kst + oK[0] + 4), ld_lds_tr4(kst + oK[1] + 4));
+          acc1 = mfma16(a1, bq, acc1);
+        }
       }
-      // lane (li, lg): row hq*16 + li of the chunk, head dims dsl*16 + 4 lg ..
-      const int r = r0q + hq * 16 + li;
-      if (r < p.rows) {
-        const int pos = pos_of(r);
-        const int hh = r - pos * G;
-        bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + dsl * 16 + lg * 4;
-        *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(acc * p.scale));
+      if constexpr (KV_W > 8) {
+        // lane (li, lg): row (w >> 1)*16 + li of the chunk, dims 32 (w & 1) + 8 lg .. +7
+        const int r = r0q + ((wave >> 1) & 1) * 16 + li;
+        if (r < p.rows) {
+          const int pos = pos_of(r);
+          const int hh = r - pos * G;
+          bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + 32 * (wave & 1) + 8 * lg;
+          st_global16(dst, pack8(acc * p.scale, acc1 * p.scale));
+        }
+      } else {
+        // lane (li, lg): row (w >> 2)*16 + li of the chunk, dims (w & 3)*16 + 4 lg ..
+        const int r = r0q + (wave >> 2) * 16 + li;
+        if (r < p.rows) {
+          const int pos = pos_of(r);
+          const int hh = r - pos * G;
+          bf16* dst = p.dq + gq.base + (int64_t)pos * gq.pos_stride + qhead + hh * 64 + (wave & 3) * 16 + lg * 4;
+          *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, pack4(acc * p.scale));
+        }
       }
     }
   };
