@@ -378,16 +378,18 @@ void attn_fwd_kernel(FwdParams p) {
           l[qt] += ls[qt];
           pb[qt] = pack8(e0[qt], e1[qt]);
         }
-        // O^T += V^T P^T.  Tile dt's operand row r is head dim 16 (r >> 2) +
-        // 4 dt + (r & 3), so that its output rows 4 lg .. 4 lg + 3 are dims
-        // 16 lg + 4 dt .. +3 and each lane ends with 16 consecutive dims of
-        // its query row (two 16-byte stores).  Lane (li, lg) receives dim
-        // 16 (li >> 2) + 4 dt + (li & 3) of keys 4 lg .. +3 and 16 + 4 lg ..
-        // +3 of the step, the keys its P^T operand holds: the lanes with li &
-        // 3 == b address the four dims from 16 b + 4 dt.
+        // O^T += V^T P^T.  Tile dt's operand row r is head dim 8 (r >> 2) +
+        // 4 (dt & 1) + 32 (dt >> 1) + (r & 3), so that its output rows 4 lg
+        // .. 4 lg + 3 are dims 8 lg + 4 (dt & 1) + 32 (dt >> 1) .. +3: each
+        // lane ends with dims 8 lg .. +7 and 32 + 8 lg .. +7 of its query
+        // row, and each of its two 16-byte stores joins the other lanes of
+        // the row into 64 contiguous bytes.  Lane (li, lg) receives dim 8
+        // (li >> 2) + 4 (dt & 1) + 32 (dt >> 1) + (li & 3) of keys 4 lg .. +3
+        // and 16 + 4 lg .. +3 of the step, the keys its P^T operand holds:
+        // the lanes with li & 3 == b address the four dims from 8 b + ....
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int kr = st * 32 + 4 * lg + (li >> 2), dcol = 16 * (li & 3) + 4 * dt;
+          const int kr = st * 32 + 4 * lg + (li >> 2), dcol = 8 * (li & 3) + 4 * (dt & 1) + 32 * (dt >> 1);
           const bf16x8 vt = join8(ld_lds_tr4(sV + k_off(kr, dcol >> 3) + (dcol & 7)),
                                   ld_lds_tr4(sV + k_off(kr + 16, dcol >> 3) + (dcol & 7)));
 #pragma unroll
@@ -409,10 +411,10 @@ void attn_fwd_kernel(FwdParams p) {
         const float lt = group4_sum(l[qt]);
         if (!qvalid[qt]) continue;
         const float inv = __builtin_amdgcn_rcpf(lt);  // (O is rounded to bf16)
-        // dims 16 lg .. 16 lg + 15 of the row
-        bf16* dst = obase + qpos[qt] * gq.pos_stride + hh[qt] * 64 + lg * 16;
+        // dims 8 lg .. +7 and 32 + 8 lg .. +7 of the row
+        bf16* dst = obase + qpos[qt] * gq.pos_stride + hh[qt] * 64 + lg * 8;
         st_global16(dst, pack8(acc[qt][0] * inv, acc[qt][1] * inv));
-        st_global16(dst + 8, pack8(acc[qt][2] * inv, acc[qt][3] * inv));
+        st_global16(dst + 32, pack8(acc[qt][2] * inv, acc[qt][3] * inv));
         if (lg == 0) lbase[qpos[qt] * gl.pos_stride + hh[qt]] = (m[qt] + __log2f(lt)) * kLn2;
       }
     }
