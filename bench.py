@@ -552,8 +552,9 @@ def main():
                     help="rollout_decode: environments generated at once")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the op shards by block / slot with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(space attention shards by block and time attention by slot, with no exchange)",
+              file=sys.stderr)
         sys.exit(2)
     if args.steps is None:
         args.steps = 200
