@@ -79,3 +79,15 @@ def test_profile_summary_maps_kernel_instances_to_ops():
     }
     for name, op in cases.items():
         assert R.op_of(name) == op, name
+
+
+def test_committed_counter_summaries_match_the_kernel_sources():
+    """The rocprofv3 summaries under profiles/ were taken on the kernels as
+    they are: every figure the bench attaches to its roofline (HBM bytes of
+    the step's ops, of the decode and of the projections; the MFMA
+    utilisation of the step's kernels) is read, none is dropped as stale."""
+    for op in ("space_fwd", "space_bwd", "time_fwd", "time_bwd"):
+        assert bench.read_traffic(op) is not None, op
+        assert bench.read_util(op) is not None, op
+    assert bench.read_traffic("time_decode", bench.TRAFFIC_FILE_DECODE) is not None
+    assert bench.read_traffic("out_proj", bench.TRAFFIC_FILE_PROJ) is not None
