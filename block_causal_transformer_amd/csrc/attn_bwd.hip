@@ -90,6 +90,13 @@ struct BwdParams {
   // part and are summed by the reduce kernel
   int split_base, split_chunk, split_keys;
   float* part;
+  // fused backward of windowed time attention over more than one key block:
+  // each problem runs as nseg workgroups, segment s owning the query rows of
+  // positions [s * seg_pos, (s + 1) * seg_pos) and the keys they see,
+  // [s * seg_pos - window + 1, (s + 1) * seg_pos) (at most seg_keys); its
+  // fp32 dK, dV partials (seg_keys keys x 128) go to part and the segment
+  // reduce kernel sums them (0 segments: not this path)
+  int nseg, seg_pos, seg_keys;
 };
 
 // ------------------------------------------------------------- dq kernel
@@ -433,11 +440,16 @@ void attn_bwd_dkv_kernel(BwdParams p) {
 
   // workgroup = (problem, block of kbl keys); one block for L <= 320.  With
   // FQ, workgroups from split_base on are halves of the last problems.
-  int ug, kb, half = -1;
+  int ug, kb, half = -1, seg = -1;
   if (FQ && (int)blockIdx.x >= p.split_base) {
     const int j = (int)blockIdx.x - p.split_base;
     ug = p.split_base + (j >> 1);
     half = j & 1;
+    kb = 0;
+  } else if (FQ && OP == OP_TIME && p.nseg > 0) {
+    // a problem's segments go to one XCD one after another (neighbouring
+    // segments share most of their keys)
+    xcd_remap(blockIdx.x, p.units * p.Hkv, p.nseg, ug, seg);
     kb = 0;
   } else {
     xcd_remap(blockIdx.x, p.units * p.Hkv, p.kvb, ug, kb);
@@ -456,8 +468,9 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int li = lane & 15, lg = lane >> 4;
-  const int kb0 = kb * p.kbl;                 // first key of the block
-  const int kend = min(p.L, kb0 + p.kbl);      // one past its last key
+  // first key of the block and one past its last key
+  const int kb0 = seg >= 0 ? max(0, seg * p.seg_pos - p.window + 1) : kb * p.kbl;
+  const int kend = seg >= 0 ? min(p.L, (seg + 1) * p.seg_pos) : min(p.L, kb0 + p.kbl);
   const int nkt = (kend - kb0 + 15) >> 4;
 
   // K and V operands of the wave's tiles, straight from global memory
@@ -595,6 +608,12 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   }
   if (half == 0) c_hi = min(c_hi, p.split_chunk);
   if (half == 1) c_lo = max(c_lo, p.split_chunk);
+  if (seg >= 0) {
+    // the segment's own rows (seg_pos * G is a whole number of chunks); the
+    // keys they see all lie in [kb0, kend), so their dQ is complete here
+    c_lo = seg * p.seg_pos * G / KV_QC;
+    c_hi = (min(p.L, (seg + 1) * p.seg_pos) * G + KV_QC - 1) / KV_QC;
+  }
   const int nchunks = c_hi;
 
   // byte offsets of this lane's LDS reads within a chunk buffer, formed once
@@ -945,6 +964,22 @@ void attn_bwd_dkv_kernel(BwdParams p) {
   if (DQ32 && nchunks > c_lo) dq_phase32(nchunks - 1);
   if (FQ && !DQ32 && nchunks > c_lo) dq_phase(nchunks - 1);
 
+  if (FQ && seg >= 0) {
+    // a segment: its fp32 partials of the keys [kb0, kend), (64 dK, 64 dV) each
+    float* dst = p.part + ((int64_t)ug * p.nseg + seg) * p.seg_keys * 128;
+#pragma unroll
+    for (int m = 0; m < TPW; ++m) {
+      const int key = kb0 + tile(m) * 16 + li;
+      if (key >= kend) continue;
+      const int64_t at = (int64_t)(key - kb0) * 128;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        *reinterpret_cast<f32x4*>(dst + at + dt * 16 + lg * 4) = dKT[m][dt];
+        *reinterpret_cast<f32x4*>(dst + at + 64 + dt * 16 + lg * 4) = dVT[m][dt];
+      }
+    }
+    return;
+  }
   if (FQ && half >= 0) {
     // a half problem: its fp32 partials, keys x (64 dK, 64 dV)
     float* dst = p.part + ((int64_t)(ug - p.split_base) * 2 + half) * p.split_keys * 128;
@@ -995,6 +1030,32 @@ __global__ __launch_bounds__(256) void attn_bwd_split_reduce_kernel(BwdParams p,
   const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
   bf16* dst = (pc < 8 ? p.dk : p.dv) + gk.base + (int64_t)key * gk.pos_stride + g * 64 + (pc & 7) * 8;
   st_global16(dst, pack8((a0 + b0) * sc, (a1 + b1) * sc));
+}
+
+// dK, dV of the segmented time backward: for each key, the fp32 partials of
+// the segments whose key range holds it (segments key / seg_pos .. (key +
+// window - 1) / seg_pos) summed in segment order, scaled (dK) and rounded to
+// bf16.  One thread per (problem, key, 8 head dims of dK or of dV).
+__global__ __launch_bounds__(256) void attn_bwd_seg_reduce_kernel(BwdParams p) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = (int64_t)p.L * 16;
+  if (idx >= (int64_t)p.units * p.Hkv * per) return;
+  const int ug = (int)(idx / per);
+  const int rem = (int)(idx - (int64_t)ug * per);
+  const int key = rem >> 4, pc = rem & 15;
+  const int u = ug / p.Hkv, g = ug - (ug / p.Hkv) * p.Hkv;
+  const UnitGeom gk = unit_geom(OP_TIME, u, p.T, p.N, p.Hkv, 64);
+  const int s0 = key / p.seg_pos, s1 = min(p.nseg - 1, (key + p.window - 1) / p.seg_pos);
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int sg = s0; sg <= s1; ++sg) {
+    const int kb0 = max(0, sg * p.seg_pos - p.window + 1);
+    const float* src = p.part + (((int64_t)ug * p.nseg + sg) * p.seg_keys + (key - kb0)) * 128 + pc * 8;
+    a0 += *reinterpret_cast<const f32x4*>(src);
+    a1 += *reinterpret_cast<const f32x4*>(src + 4);
+  }
+  const float sc = pc < 8 ? p.scale : 1.0f;
+  bf16* dst = (pc < 8 ? p.dk : p.dv) + gk.base + (int64_t)key * gk.pos_stride + g * 64 + (pc & 7) * 8;
+  st_global16(dst, pack8(a0 * sc, a1 * sc));
 }
 
 // Number of compute units of the current device (0 if none).
@@ -1064,8 +1125,48 @@ size_t bwd_split_bytes(const AttnDims& d) {
   return (size_t)sp.count * 2 * sp.keys * 128 * sizeof(float);
 }
 
+// Windowed time attention longer than one key block: the fused backward
+// runs each problem as segments of seg_pos query positions, whose rows see
+// at most seg_pos + W - 1 <= 320 keys, so that S and dP are formed once (the
+// two-kernel path forms them in both kernels) and only the dK, dV partials
+// of overlapping key ranges are summed afterwards.  seg_pos * G must be a
+// whole number of 32-row chunks (so that no chunk is shared by two
+// segments); segments shorter than kMinSegPos positions are not worth it
+// (their key ranges overlap too much): the two-kernel path is used then.
+constexpr int kMinSegPos = 128;
+
+struct SegPlan {
+  int nseg = 0, pos = 0, keys = 0;
+};
+
+SegPlan plan_segments(const AttnDims& d) {
+  SegPlan sp;
+  if (d.op != OP_TIME || d.window <= 0 || d.no_seg || !bwd_uses_mfma(d) || uses_short(d)) return sp;
+  const int L = d.T, W = d.window, G = d.Hq / d.Hkv;
+  if (L <= kBwdKeyBlock) return sp;
+  int gcd = G, b = KV_QC;
+  while (b) {
+    const int t = gcd % b;
+    gcd = b;
+    b = t;
+  }
+  const int unit = KV_QC / gcd;  // positions per whole number of chunks
+  const int R = ((kBwdKeyBlock - W + 1) / unit) * unit;
+  if (R < kMinSegPos || R >= L) return sp;
+  sp.pos = R;
+  sp.nseg = (L + R - 1) / R;
+  sp.keys = ((std::min(L, R + W - 1) + 15) / 16) * 16;
+  return sp;
+}
+
+size_t bwd_seg_bytes(const AttnDims& d) {
+  const SegPlan sp = plan_segments(d);
+  return (size_t)d.B * d.N * d.Hkv * sp.nseg * sp.keys * 128 * sizeof(float);
+}
+
 size_t bwd_bf16_workspace_bytes(const AttnDims& d) {
-  return (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
+  const size_t seg = bwd_seg_bytes(d);
+  return seg > 0 ? seg : (size_t)d.B * d.T * d.N * d.Hq * sizeof(float);
 }
 
 // ------------------------------------------------- static scratch (no-alloc)
@@ -1131,6 +1232,29 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
   p.poison = d.poison;
   if (p.G > 256 || (long)p.rows >= (1L << 21)) return hipErrorInvalidValue;
   const long problems = (long)p.units * p.Hkv;
+  p.split_base = 0x7fffffff;
+  p.split_chunk = p.split_keys = 0;
+  p.nseg = p.seg_pos = p.seg_keys = 0;
+
+  // windowed time attention longer than one key block: the fused kernel
+  // (three tile slots, dQ formed in it) per segment, then the partials' sum
+  const SegPlan sg = plan_segments(d);
+  if (sg.nseg > 0) {
+    if (!workspace) return hipErrorInvalidValue;
+    p.nseg = sg.nseg;
+    p.seg_pos = sg.pos;
+    p.seg_keys = sg.keys;
+    p.kvb = 1;
+    p.kbl = sg.keys;
+    p.part = static_cast<float*>(workspace);
+    const long grid = problems * sg.nseg;
+    const long red = (problems * p.L * 16 + 255) / 256;
+    if (grid > 0x7fffffff || red > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), dim3((unsigned)grid), dim3(kv_waves<3>() * 64),
+                       0, stream, p);
+    hipLaunchKernelGGL(attn_bwd_seg_reduce_kernel, dim3((unsigned)red), dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
 
   // dq kernel: one workgroup per CU (LDS), rows split so the grid covers the
   // CUs a few times over

@@ -9,6 +9,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "bca.h"
@@ -148,10 +149,11 @@ int do_fwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, 
 
 int do_bwd(int op, const bca_shape* shape, const bca_mask* mask, const void* q, const void* k,
            const void* v, const void* o, const float* lse, const void* dout, void* dq, void* dk,
-           void* dv, void* workspace, size_t ws_bytes, void* stream) {
+           void* dv, void* workspace, size_t ws_bytes, void* stream, bool segments = true) {
   bca::AttnDims d;
   int st = validate(op, shape, mask, &d);
   if (st) return st;
+  d.no_seg = segments ? 0 : 1;
   const char* names[] = {"q", "k", "v", "o", "lse", "dout", "dq", "dk", "dv"};
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   st = check_ptrs(names, ptrs, 9);
@@ -191,7 +193,16 @@ int do_bwd_noalloc(int op, const bca_shape* shape, const bca_mask* mask, const v
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   st = check_ptrs(names, ptrs, 9);
   if (st) return st;
-  const size_t need = workspace_bytes(d);
+  // windowed time attention over more than one key block runs as segments
+  // whose dK, dV partials need more workspace than the Delta rows of the
+  // two-kernel path; when they do not fit the scratch, the latter is used
+  size_t need = workspace_bytes(d);
+  bool segments = true;
+  if (need > bca::kNoAllocScratchBytes) {
+    d.no_seg = 1;
+    need = workspace_bytes(d);
+    segments = false;
+  }
   if (need > bca::kNoAllocScratchBytes)
     return fail(BCA_ERR_INVALID_ARG,
                 "this shape needs %zu bytes of workspace; the static scratch holds %zu "
@@ -203,7 +214,7 @@ int do_bwd_noalloc(int op, const bca_shape* shape, const bca_mask* mask, const v
     if (e != hipSuccess)
       return fail(BCA_ERR_HIP, "static scratch lookup: %s", hipGetErrorString(e));
   }
-  return do_bwd(op, shape, mask, q, k, v, o, lse, dout, dq, dk, dv, ws, need, stream);
+  return do_bwd(op, shape, mask, q, k, v, o, lse, dout, dq, dk, dv, ws, need, stream, segments);
 }
 
 int do_decode_fwd(const bca_shape* shape, const bca_mask* mask, const void* q, const void* kc,
@@ -372,7 +383,16 @@ size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape) {
     g_last_error = saved;
     return 0;
   }
-  return workspace_bytes(d);
+  size_t need = workspace_bytes(d);
+  // the need depends on the time op's window, which the query does not
+  // take: the largest over all windows.  Windowed time attention over more
+  // than one key block runs as segments of at least 128 positions, whose
+  // partials take the most room at exactly 128 (window 193).
+  if (op == BCA_OP_TIME) {
+    d.window = 193;
+    need = std::max(need, workspace_bytes(d));
+  }
+  return need;
 }
 
 const char* bca_status_string(int status) {

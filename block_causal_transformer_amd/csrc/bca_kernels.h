@@ -21,6 +21,10 @@ struct AttnDims {
   // debug: fill the kernels' LDS with NaN bit patterns before staging, so
   // that a read of LDS no thread wrote shows up in the results
   int poison = 0;
+  // backward: do not run windowed time attention over more than one key
+  // block as segments of the fused kernel (whose fp32 dK, dV partials need
+  // more workspace) but as the two-kernel path (Delta workspace only)
+  int no_seg = 0;
 };
 
 // AttnDims::op of the decode call (the kernels' OP_DECODE).

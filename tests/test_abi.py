@@ -132,7 +132,15 @@ def test_workspace_query_and_check(lib):
     assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=16, N=1432, Hq=16, Hkv=16)) == 0
     # longer problems: one fp32 Delta per (query, head)
     assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_SPACE, good_shape(N=321)) == 1 * 4 * 321 * 4 * 4
-    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=1024)) == 1 * 1024 * 10 * 4 * 4
+    # ... except windowed time attention, which runs as segments of at least
+    # 128 positions whose fp32 dK, dV partials (keys of the segment's range,
+    # at most 320, x 128) take more: the query takes no window and returns
+    # the most any window needs (segments of exactly 128 positions): 10 slots
+    # x 2 KV heads x 8 segments x 320 keys x 512 bytes
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=1024)) == 10 * 2 * 8 * 320 * 512
+    # at 330 frames (3 segments of 128; a segment's range is the 320 keys
+    # before its end), still more than Delta's 330 * 10 * 4 * 4 bytes
+    assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(T=330)) == 10 * 2 * 3 * 320 * 512
     # the space op's length is N and the time op's T
     assert ops.bca_bwd_workspace_bytes(ops.BCA_OP_TIME, good_shape(N=1432, T=8)) == 0
     # the generic VALU path (head_dim 32, fp32) always uses it
@@ -147,6 +155,17 @@ def test_workspace_query_and_check(lib):
     assert rc == ops.BCA_ERR_INVALID_ARG and "workspace" in ops.bca_last_error()
     rc = bwd_call("space", s, ops.BcaMask(0, 0, 0, 0, 0.0), ws=None, ws_bytes=need)
     assert rc == ops.BCA_ERR_INVALID_ARG
+    # a call needs what its own window needs: with a 192-frame window the
+    # segments' partials (the query's figure), unbounded causal only Delta
+    t = good_shape(T=1024)
+    seg = 10 * 2 * 8 * 320 * 512
+    rc = bwd_call("time", t, ops.BcaMask(1, 192, 0, 0, 0.0), ws=FAKE, ws_bytes=seg - 1)
+    assert rc == ops.BCA_ERR_INVALID_ARG and str(seg) in ops.bca_last_error()
+    rc = bwd_call("time", t, ops.BcaMask(1, 0, 0, 0, 0.0), ws=FAKE, ws_bytes=1024 * 10 * 4 * 4 - 1)
+    assert rc == ops.BCA_ERR_INVALID_ARG and str(1024 * 10 * 4 * 4) in ops.bca_last_error()
+    # a window too long for segments of 128 positions: Delta
+    rc = bwd_call("time", t, ops.BcaMask(1, 200, 0, 0, 0.0), ws=FAKE, ws_bytes=1024 * 10 * 4 * 4 - 1)
+    assert rc == ops.BCA_ERR_INVALID_ARG and str(1024 * 10 * 4 * 4) in ops.bca_last_error()
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

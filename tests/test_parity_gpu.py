@@ -221,3 +221,38 @@ def test_parity_unit_dout_on_floor(w):
     floor = {k: U.bf16_metrics(fl[k], want[k]) for k in ("o", "dq", "dk", "dv")}
     print("floor", {k: round(v["vs_rounded_excess"], 5) for k, v in floor.items()})
     print(U.assert_close(w, got, want, w.name, floor=floor))
+
+
+# Windowed time attention over more than one 320-key block runs the fused
+# backward per segment of query positions (segments of at least 128
+# positions whose rows see at most 320 keys) and sums the segments' dK, dV
+# partials; a window too long for such segments keeps the two-kernel path.
+# G = 10 at unit dO puts dK, dV on the method's precision floor (as config 4
+# does), so the bars move to that floor evaluated on the same inputs.
+SEGMENTED = [
+    C.Workload("seg_time_T400_G10_W192", "time", 1, 400, 2, 30, 3, 64, "bf16", 192, 0, 0, 1.0, 9401),
+    C.Workload("seg_time_T700_G10_W64", "time", 1, 700, 1, 30, 3, 64, "bf16", 64, 0, 0, 1.0, 9402),
+    C.Workload("seg_time_T500_MHA_W100", "time", 1, 500, 2, 4, 4, 64, "bf16", 100, 0, 0, 1.0, 9403),
+    C.Workload("seg_time_T600_G4_W193", "time", 1, 600, 1, 8, 2, 64, "bf16", 193, 0, 0, 1.0, 9404),
+    C.Workload("seg_time_T331_G3_W190", "time", 2, 331, 1, 6, 2, 64, "bf16", 190, 0, 0, 1.0, 9405),
+    C.Workload("twokernel_time_T450_G10_W200", "time", 1, 450, 1, 30, 3, 64, "bf16", 200, 0, 0, 1.0, 9406),
+]
+
+
+@pytest.mark.parametrize("w", SEGMENTED, ids=[w.name for w in SEGMENTED])
+def test_parity_segmented_time(w):
+    _needs_gpu()
+    import os
+    import sys
+    golden = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    if golden not in sys.path:
+        sys.path.insert(0, golden)
+    import precision_floor as PF
+    print("case", w.name, flush=True)
+    inp = gen.make_inputs(w)
+    got = U.run_hip(w, inp)
+    want = U.run_oracle(w, inp)
+    fl = PF.emulate(w, inp)
+    floor = {k: U.bf16_metrics(fl[k], want[k]) for k in ("o", "dq", "dk", "dv")}
+    print("floor", {k: round(v["vs_rounded_excess"], 5) for k, v in floor.items()})
+    print(U.assert_close(w, got, want, w.name, floor=floor))
