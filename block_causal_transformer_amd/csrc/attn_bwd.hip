@@ -1250,8 +1250,12 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
     const long grid = problems * sg.nseg;
     const long red = (problems * p.L * 16 + 255) / 256;
     if (grid > 0x7fffffff || red > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), dim3((unsigned)grid), dim3(kv_waves<3>() * 64),
-                       0, stream, p);
+    if (p.G == 10)  // the dynamics model's 30 query heads over 3
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true, 10>), dim3((unsigned)grid),
+                         dim3(kv_waves<3>() * 64), 0, stream, p);
+    else
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), dim3((unsigned)grid),
+                         dim3(kv_waves<3>() * 64), 0, stream, p);
     hipLaunchKernelGGL(attn_bwd_seg_reduce_kernel, dim3((unsigned)red), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
@@ -1316,6 +1320,8 @@ hipError_t launch_attn_bwd_bf16(const AttnDims& d, const void* q, const void* k,
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true, 10>), g2d, bw, 0, stream, p);
     else if (tpw == 1)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 1, true>), g2d, bw, 0, stream, p);
+    else if (fq && p.G == 10)
+      hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true, 10>), g2d, b8, 0, stream, p);
     else if (fq)
       hipLaunchKernelGGL((attn_bwd_dkv_kernel<OP_TIME, 3, true>), g2d, b8, 0, stream, p);
     else if (tpw == 2)
