@@ -180,9 +180,12 @@ int time_attn_decode_fwd(const bca_shape* shape, const bca_mask* mask, const voi
  * It calls no hipMalloc, hipFree or allocating library routine.  The array
  * holds 64 MiB per GPU (kept until the process ends), enough for
  * B*T*N*Hq <= 2^24 (query, head) rows or the split partials of up to 128
- * problems; shapes that need more workspace
- * (bca_bwd_workspace_bytes(BCA_OP_TIME, shape) > 64 MiB) are refused with
- * BCA_ERR_INVALID_ARG before any launch.  Every call on one GPU uses that
+ * problems.  Where time_attn_bwd would run windowed attention over more
+ * than 320 frames as segments whose partials do not fit the array, this
+ * call runs the two-kernel backward (Delta rows only), whose results agree
+ * with time_attn_bwd's to rounding, not bit for bit.  Shapes whose need
+ * still exceeds 64 MiB are refused with BCA_ERR_INVALID_ARG before any
+ * launch.  Every call on one GPU uses that
  * GPU's one array: calls that overlap in time on one GPU (other streams,
  * other threads) race and must be serialized by the caller.  Nothing in the
  * array needs to start at any value.  Other arguments, ownership and errors
@@ -192,20 +195,28 @@ int time_attn_bwd_noalloc(const bca_shape* shape, const bca_mask* mask, const vo
                           const void* dout, void* dq, void* dk, void* dv, void* stream);
 
 /* Bytes of device workspace the backward of `op` (BCA_OP_SPACE or
- * BCA_OP_TIME) needs for `shape` on the current device.  On the bf16
- * head_dim-64 path with an attended length (N for space, T for time) of at
- * most 320, every problem (a block or slot and a KV head) is one key block
- * and one kernel forms dQ, dK and dV; it runs one workgroup per problem and
- * compute unit, so the problems pass through the device in rounds.  When
- * there are more problems than compute units and the last round is at most
- * half full, that round's problems each run as two workgroups (one per half
- * of the query rows), whose fp32 dK, dV partials, 2 * ceil(L/16)*16 * 128 * 4
- * bytes per such problem, go to the workspace and are summed in a fixed
- * order by a second kernel; otherwise this path needs 0 bytes.  With longer
- * attended lengths the backward needs one fp32 Delta = rowsum(dO * O) per
- * (query, head), B*T*N*Hq*4 bytes, which its first kernel writes and its
- * second reads.  The op is an argument because the attended length depends
- * on it.  Returns 0 for an invalid shape or op. */
+ * BCA_OP_TIME) needs for `shape` on the current device, for any mask.  On
+ * the bf16 head_dim-64 path with an attended length (N for space, T for
+ * time) of at most 320, every problem (a block or slot and a KV head) is one
+ * key block and one kernel forms dQ, dK and dV; it runs one workgroup per
+ * problem and compute unit, so the problems pass through the device in
+ * rounds.  When there are more problems than compute units and the last
+ * round is at most half full, that round's problems each run as two
+ * workgroups (one per half of the query rows), whose fp32 dK, dV partials,
+ * 2 * ceil(L/16)*16 * 128 * 4 bytes per such problem, go to the workspace and
+ * are summed in a fixed order by a second kernel; otherwise this path needs
+ * 0 bytes.  With longer attended lengths the backward needs one fp32
+ * Delta = rowsum(dO * O) per (query, head), B*T*N*Hq*4 bytes, which its
+ * first kernel writes and its second reads; except time attention with a
+ * window W whose segments of R positions (the largest multiple of
+ * 32 / gcd(G, 32) with R + W - 1 <= 320) hold at least 128: it runs as
+ * ceil(T/R) segments per problem, each forming dQ of its rows and writing
+ * fp32 dK, dV partials of the keys its rows see, ceil(min(T, R + W - 1)/16)
+ * * 16 * 128 * 4 bytes per segment, summed per key by a second kernel.  The
+ * query takes no window and returns the most any window needs (segments of
+ * 128 positions when T > 320, or Delta when that is larger); a call checks
+ * the need of its own mask.  The op is an argument because the attended
+ * length depends on it.  Returns 0 for an invalid shape or op. */
 size_t bca_bwd_workspace_bytes(int op, const bca_shape* shape);
 
 /* ---- projections beside attention ----
