@@ -5,7 +5,8 @@ needing the scratch (more than 320 frames: the Delta workspace is used), a
 shape whose split last round puts its partials there, plus a shape that
 needs none and one the scratch cannot hold.  Same kernels, so the
 results must be bitwise equal; the first call is also checked against the
-oracle."""
+oracle.  A shape whose segment partials exceed the scratch takes the
+two-kernel path instead and agrees to rounding."""
 import numpy as np
 import pytest
 
@@ -54,6 +55,30 @@ def test_noalloc_matches_allocating_backward_twice():
             want = U.run_oracle(w, inp)
             print(U.assert_close(w, {"dq": U.to_np(got[0]), "dk": U.to_np(got[1]), "dv": U.to_np(got[2])},
                                  want, w.name + " noalloc"))
+
+
+def test_noalloc_two_kernel_fallback():
+    """Windowed time attention over 1024 frames with 80 problems: the
+    segmented backward's fp32 partials (80 x 8 segments x 320 keys x 512
+    bytes = 105 MB) do not fit the 64 MiB scratch, so the no-allocation call
+    runs the two-kernel backward (Delta, 1 MB); the gradients are then those
+    of time_attn_bwd up to rounding (both paths are checked against the
+    oracle elsewhere), within the bf16 bars of the parity tests."""
+    _needs_gpu()
+    w = C.Workload("time_T1024_N40_W192", "time", 1, 1024, 40, 6, 2, 64, "bf16", 192, 0, 0, 1.0, 9304)
+    print("case", w.name, flush=True)
+    inp = gen.make_inputs(w)
+    ref, got = _both(w, inp)
+    same = []
+    for name, a, b in zip(("dq", "dk", "dv"), ref, got):
+        a, b = U.to_np(a), U.to_np(b)
+        excess = float(np.max(np.abs(a - b) - np.maximum(2e-2, 2 * U.half_ulp_bf16(a))))
+        rel = float(np.linalg.norm(a - b) / np.linalg.norm(a))
+        print(name, "excess %.3g rel %.3g" % (excess, rel))
+        assert excess <= 0 and rel <= 5e-3, name
+        same.append(np.array_equal(a, b))
+    # (the other path: its sums in another order leave other roundings)
+    assert not all(same), "expected the two-kernel path's rounding"
 
 
 def test_noalloc_split_last_round():
