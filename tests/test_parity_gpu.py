@@ -236,6 +236,9 @@ SEGMENTED = [
     C.Workload("seg_time_T600_G4_W193", "time", 1, 600, 1, 8, 2, 64, "bf16", 193, 0, 0, 1.0, 9404),
     C.Workload("seg_time_T331_G3_W190", "time", 2, 331, 1, 6, 2, 64, "bf16", 190, 0, 0, 1.0, 9405),
     C.Workload("twokernel_time_T450_G10_W200", "time", 1, 450, 1, 30, 3, 64, "bf16", 200, 0, 0, 1.0, 9406),
+    # the shortest windows: segments of 320 positions
+    C.Workload("seg_time_T400_G6_W1", "time", 1, 400, 2, 12, 2, 64, "bf16", 1, 0, 0, 1.0, 9407),
+    C.Workload("seg_time_T700_G10_W2", "time", 1, 700, 1, 30, 3, 64, "bf16", 2, 0, 0, 1.0, 9408),
 ]
 
 
