@@ -55,6 +55,15 @@
 // that the causal / window ranges make invisible are never visited.  For
 // long problems the split costs two more matmul passes (S and dP are formed
 // in both kernels) in exchange for no cross-workgroup sum of dQ.
+//
+// Windowed time attention over more than 320 frames avoids the split: the
+// fused dkv kernel runs each problem as segments of R query positions (R +
+// W - 1 <= 320, R * G a whole number of 32-row chunks).  A segment's rows see
+// only the keys [s R - W + 1, (s + 1) R), which fit one block, so it forms
+// their dQ completely; its dK, dV cover keys that neighbouring segments'
+// rows see too, so they go out as fp32 partials and the segment reduce
+// kernel adds, per key, the partials of the segments that hold it in
+// segment order (deterministic).
 #include <algorithm>
 #include <mutex>
 
