@@ -57,6 +57,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 TRAFFIC_FILE_DECODE = os.path.join(ROOT, "profiles", "hbm_traffic_rollout_decode.txt")
 TRAFFIC_FILE_PROJ = os.path.join(ROOT, "profiles", "hbm_traffic_projections.txt")
+TRAFFIC_FILE_LONG = os.path.join(ROOT, "profiles", "hbm_traffic_long_time.txt")
 UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_utilisation.txt")
 
 
@@ -702,7 +703,8 @@ def main_step(args):
     d = per_op[dom]
     roof = roofline_of(d["flop"], d["min_bytes"], d["ms"])
     roof["kernel"] = dom + " (" + KERNELS[d["op"]] + ")"
-    roof["traffic"] = read_traffic(dom) if args.workload == "train_step" else None
+    roof["traffic"] = (read_traffic(dom) if args.workload == "train_step" else
+                       read_traffic(d["op"], TRAFFIC_FILE_LONG) if args.workload == "long_time" else None)
     if args.workload == "train_step":
         # rocprofv3 counters of the same kernels (MFMA busy share of the
         # SIMDs' cycles), from the committed summary when it matches the sources

@@ -40,6 +40,7 @@ OPS = [
     (r"attn_bwd_dkv_kernel<1[,>]", "time_bwd"),
     (r"attn_bwd_split_reduce_kernel<0>", "space_bwd"),
     (r"attn_bwd_split_reduce_kernel<1>", "time_bwd"),
+    (r"attn_bwd_seg_reduce_kernel", "time_bwd"),
     (r"rstd_rows_kernel", "qkv_proj"),
     (r"fold_gain_kernel", "qkv_proj"),
     (r"gemm256_kernel<0[,>]", "qkv_proj"),
@@ -137,7 +138,12 @@ def cmd_stats(args):
                     "ms_per_step %.4f:" % d["ms_per_step"], "",
                     "| op | events (us) | kernel trace (us) |", "|---|---|---|"]
             for op, v in d.get("ops", {}).items():
-                kt = per_op.get({"space_fwd_block": "space_fwd"}.get(op, op))
+                # a workload's op names may carry its config as a prefix
+                # ("4L_time_bwd"); the kernels' op is the rest
+                base = {"space_fwd_block": "space_fwd"}.get(op, op)
+                if base not in per_op and "_" in base and base.split("_", 1)[1] in per_op:
+                    base = base.split("_", 1)[1]
+                kt = per_op.get(base)
                 out.append("| %s | %.1f | %s |" % (op, 1e3 * v["ms"], "%.1f" % kt if kt else "-"))
     out.append("")
     with open(args.out, "w") as f:

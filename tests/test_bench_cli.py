@@ -91,3 +91,4 @@ def test_committed_counter_summaries_match_the_kernel_sources():
         assert bench.read_util(op) is not None, op
     assert bench.read_traffic("time_decode", bench.TRAFFIC_FILE_DECODE) is not None
     assert bench.read_traffic("out_proj", bench.TRAFFIC_FILE_PROJ) is not None
+    assert bench.read_traffic("time_bwd", bench.TRAFFIC_FILE_LONG) is not None
