@@ -19,8 +19,9 @@
 // of PARTS partial dot products over xor-shuffles.  K and V (and in the
 // backward Q, dO, P and dS) are staged in the wave's own LDS slice.
 //
-//  short_fwd_kernel: scores, masked softmax in the log2 domain, O = P V and
-//      LSE (natural log) per row.
+//  short_fwd_kernel: every score (bf16 dot products on v_dot2), the masked
+//      softmax in the log2 domain, O = P V (P as bf16, V transposed in LDS)
+//      and LSE (natural log) per row.
 //  short_bwd_kernel: phase A, lane = (row, part): P from the stored LSE,
 //      Delta = rowsum(dO * O), dP = dO V^T, dS = P (dP - Delta), dQ = scale
 //      dS K; phase B, lane = (key, part): dV = P^T dO, dK = scale dS^T Q,
@@ -116,14 +117,30 @@ __device__ __forceinline__ float dot_lds(const float* f, const bf16* row) {
   return s;
 }
 
+// The sum of the products of two bf16 vectors' 8 element pairs, added to s
+// (v_dot2_f32_bf16: each bf16 product is exact in fp32).
+__device__ __forceinline__ float dot8(const bf16x8& a, const bf16x8& b, float s) {
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), s, false);
+  return s;
+}
+
+// Two passes over the problem's (at most 32) keys: every score first (the
+// lane's partial dot products on v_dot2, summed over the row's lanes), then
+// the row maximum, the exps and their sum, then O = P V with P rounded to
+// bf16 (the matmul operand precision of the method, as on the MFMA path)
+// and V read transposed from LDS, so that each output column is a bf16 dot
+// product along the keys.
 template <int OP, int RP, int LP>
 __global__ __launch_bounds__(SWAVES * 64) void short_fwd_kernel(ShortParams p) {
   constexpr int PARTS = 64 / RP, DP = SD / PARTS;
   __shared__ __attribute__((aligned(16))) bf16 sK[SWAVES][LP * SD];
-  __shared__ __attribute__((aligned(16))) bf16 sV[SWAVES][LP * SD];
+  __shared__ __attribute__((aligned(16))) bf16 sVt[SWAVES][SD * LP];  // [column][key]
   if (p.poison) {
     poison_lds(sK, sizeof(sK), threadIdx.x, SWAVES * 64);
-    poison_lds(sV, sizeof(sV), threadIdx.x, SWAVES * 64);
+    poison_lds(sVt, sizeof(sVt), threadIdx.x, SWAVES * 64);
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
@@ -134,9 +151,23 @@ __global__ __launch_bounds__(SWAVES * 64) void short_fwd_kernel(ShortParams p) {
   const UnitGeom gq = unit_geom(OP, u, p.T, p.N, p.Hq, SD);
   const UnitGeom gk = unit_geom(OP, u, p.T, p.N, p.Hkv, SD);
   const UnitGeom gl = unit_geom(OP, u, p.T, p.N, p.Hq, 1);
-  if (live)
-    stage_kv<LP>(p.k + gk.base + (int64_t)g * SD, p.v + gk.base + (int64_t)g * SD, gk.pos_stride,
-                 p.L, lane, sK[wave], sV[wave]);
+  if (live) {
+    // K row-major, V transposed (rows past L are zero)
+    const bf16* kb = p.k + gk.base + (int64_t)g * SD;
+    const bf16* vb = p.v + gk.base + (int64_t)g * SD;
+#pragma unroll
+    for (int it = 0; it < LP / 8; ++it) {
+      const int j = it * 8 + (lane >> 3), c = (lane & 7) * 8;
+      bf16x8 a = zero8(), b = zero8();
+      if (j < p.L) {
+        a = ld_global16(kb + (int64_t)j * gk.pos_stride + c);
+        b = ld_global16(vb + (int64_t)j * gk.pos_stride + c);
+      }
+      st_lds16(sK[wave] + j * SD + c, a);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sVt[wave][(c + t) * LP + j] = b[t];
+    }
+  }
   __syncthreads();
   if (!live) return;
 
@@ -144,37 +175,52 @@ __global__ __launch_bounds__(SWAVES * 64) void short_fwd_kernel(ShortParams p) {
   const bool row_ok = r < p.R;
   const int pos = row_ok ? r / p.G : 0, hd = g * p.G + (row_ok ? r % p.G : 0);
   const int64_t qoff = gq.base + (int64_t)pos * gq.pos_stride + (int64_t)hd * SD + part * DP;
-  float qf[DP];
-  load_f32<DP>(p.q + qoff, qf);
+  bf16x8 qv[DP / 8];
+#pragma unroll
+  for (int c = 0; c < DP / 8; ++c) qv[c] = ld_global16(p.q + qoff + c * 8);
   const MaskDesc md{OP, p.L, p.window, p.agent_begin, p.agent_count};
   const float c2 = p.scale * kLog2e;
-  // online softmax over the keys (log2 domain); the partial dot products are
-  // summed by every lane (shuffles) before the per-row visibility branch
-  float m = -INFINITY, l = 0.f;
+  float sc[LP];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < LP; ++j) {
+    const bf16* kr = sK[wave] + j * SD + part * DP;
+    float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < DP / 8; c += 2) {
+      d0 = dot8(qv[c], ld_lds16(kr + c * 8), d0);
+      if (c + 1 < DP / 8) d1 = dot8(qv[c + 1], ld_lds16(kr + (c + 1) * 8), d1);
+    }
+    const float d = part_sum<PARTS>(d0 + d1);
+    sc[j] = (j < p.L && visible_op<OP>(md, pos, j)) ? d * c2 : -INFINITY;
+    m = fmaxf(m, sc[j]);
+  }
+  // every row sees at least its own position, so m is finite
+  float l = 0.f;
+#pragma unroll
+  for (int j = 0; j < LP; ++j) {
+    sc[j] = fast_exp2(sc[j] - m);
+    l += sc[j];
+  }
+  bf16x8 pb[LP / 8];
+#pragma unroll
+  for (int i = 0; i < LP / 8; ++i)
+    pb[i] = pack8(f32x4{sc[8 * i], sc[8 * i + 1], sc[8 * i + 2], sc[8 * i + 3]},
+                  f32x4{sc[8 * i + 4], sc[8 * i + 5], sc[8 * i + 6], sc[8 * i + 7]});
+  const float inv = 1.f / l;
   float acc[DP];
 #pragma unroll
-  for (int c = 0; c < DP; ++c) acc[c] = 0.f;
-#pragma unroll 2
-  for (int j = 0; j < p.L; ++j) {
-    const float d = part_sum<PARTS>(dot_lds<DP>(qf, sK[wave] + j * SD + part * DP));
-    if (visible_op<OP>(md, pos, j)) {
-      const float sj = d * c2, mn = fmaxf(m, sj);
-      const float a = fast_exp2(m - mn), e = fast_exp2(sj - mn);  // m = -inf: a = 0
-      l = __builtin_fmaf(l, a, e);
-      m = mn;
-      const bf16* vr = sV[wave] + j * SD + part * DP;
+  for (int c = 0; c < DP; ++c) {
+    const bf16* vr = sVt[wave] + (part * DP + c) * LP;
+    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-      for (int c = 0; c < DP; c += 8) {
-        const bf16x8 x = ld_lds16(vr + c);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc[c + t] = __builtin_fmaf(acc[c + t], a, e * (float)x[t]);
-      }
+    for (int i = 0; i < LP / 8; i += 2) {
+      a0 = dot8(pb[i], ld_lds16(vr + i * 8), a0);
+      if (i + 1 < LP / 8) a1 = dot8(pb[i + 1], ld_lds16(vr + (i + 1) * 8), a1);
     }
+    acc[c] = (a0 + a1) * inv;
   }
-  const float inv = 1.f / l;
   if (!row_ok) return;
-#pragma unroll
-  for (int c = 0; c < DP; ++c) acc[c] *= inv;
   store_bf16<DP>(p.out0 + qoff, acc);
   if (part == 0) p.lse_out[gl.base + (int64_t)pos * gl.pos_stride + hd] = (m + log2f(l)) * kLn2;
 }
