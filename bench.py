@@ -638,7 +638,12 @@ def main_step(args):
         if rc != 0:
             raise RuntimeError("%s %s: %s" % (name, direction, ops.bca_last_error()))
 
-    seq = [(w.name, d) for w in wls for d in ("fwd", "bwd")]
+    # Every layer's forward, then every backward in the same layer order: an
+    # op's forward and backward are then separated by the other layers' ops,
+    # which move far more than the 256 MB MALL, so no backward re-reads its
+    # inputs (or the O its forward just wrote) from that cache; the next
+    # step's forwards come after every other layer's backward.
+    seq = [(w.name, "fwd") for w in wls] + [(w.name, "bwd") for w in wls]
     if args.workload == "train_step":
         labels = {("3", "fwd"): "space_fwd", ("3", "bwd"): "space_bwd",
                   ("4", "fwd"): "time_fwd", ("4", "bwd"): "time_bwd"}
@@ -737,6 +742,7 @@ def main_step(args):
         "dtype": "bf16",
         "data": "synthetic",
         "config": cfg,
+        "order": [labels[k] for k in seq],
         "pct_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "ops": {k: {kk: vv for kk, vv in v.items() if kk not in ("flop", "min_bytes", "op")}
                 for k, v in per_op.items()},
