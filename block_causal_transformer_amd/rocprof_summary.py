@@ -41,6 +41,11 @@ OPS = [
     (r"attn_bwd_split_reduce_kernel<0>", "space_bwd"),
     (r"attn_bwd_split_reduce_kernel<1>", "time_bwd"),
     (r"attn_bwd_seg_reduce_kernel", "time_bwd"),
+    # one wave per short problem (template argument 0 = space, 1 = time)
+    (r"short_fwd_kernel<0[,>]", "space_fwd"),
+    (r"short_fwd_kernel<1[,>]", "time_fwd"),
+    (r"short_bwd_kernel<0[,>]", "space_bwd"),
+    (r"short_bwd_kernel<1[,>]", "time_bwd"),
     (r"rstd_rows_kernel", "qkv_proj"),
     (r"fold_gain_kernel", "qkv_proj"),
     (r"gemm256_kernel<0[,>]", "qkv_proj"),
@@ -137,14 +142,26 @@ def cmd_stats(args):
             out += ["", "`bench.py`'s HIP-event average per op in the same (profiled) run, "
                     "ms_per_step %.4f:" % d["ms_per_step"], "",
                     "| op | events (us) | kernel trace (us) |", "|---|---|---|"]
+            bases = {}
             for op, v in d.get("ops", {}).items():
                 # a workload's op names may carry its config as a prefix
                 # ("4L_time_bwd"); the kernels' op is the rest
                 base = {"space_fwd_block": "space_fwd"}.get(op, op)
                 if base not in per_op and "_" in base and base.split("_", 1)[1] in per_op:
                     base = base.split("_", 1)[1]
+                bases.setdefault(base, []).append((op, 1e3 * v["ms"]))
                 kt = per_op.get(base)
                 out.append("| %s | %.1f | %s |" % (op, 1e3 * v["ms"], "%.1f" % kt if kt else "-"))
+            shared = {b: ev for b, ev in bases.items() if len(ev) > 1 and b in per_op}
+            if shared:
+                # several configs run the same kernels: the trace averages
+                # over all their calls, so compare with the events' mean
+                out += ["", "Ops whose kernels serve several configs (the kernel trace averages "
+                        "over all their calls; the events' mean over those configs beside it):", "",
+                        "| op | configs | events, mean (us) | kernel trace (us) |", "|---|---|---|---|"]
+                for b, ev in shared.items():
+                    out.append("| %s | %s | %.1f | %.1f |" % (
+                        b, ", ".join(o for o, _ in ev), sum(t for _, t in ev) / len(ev), per_op[b]))
     out.append("")
     with open(args.out, "w") as f:
         f.write("\n".join(out))
